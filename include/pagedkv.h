@@ -1,0 +1,147 @@
+/*
+ * pagedkv.h -- C ABI of a gfx950 (MI355X) library for attention over a paged KV cache.
+ *
+ * The method (pages cited by title and section):
+ *   - Serving-engine KV page (ttlab, "LLM KV cache 02"), section 2 "PagedAttention",
+ *     subsection "blocks and block table": K/V live in fixed 16-token physical blocks
+ *     placed anywhere in a pool; each request maps logical blocks to physical ones
+ *     through its block table; a new block is taken when the last one fills; the
+ *     attention kernel follows the table and must give the contiguous-cache result.
+ *   - Same page, subsection "block sharing": several tables may name one block.
+ *   - "How inference engines actually work" page (xiaohu-jiedu), KV-cache section: each
+ *     step computes K/V only for the new tokens and reads the rest from the cache;
+ *     Chunked Prefill subsection: a long prompt runs as consecutive slices mixed with
+ *     other requests' single decode tokens in one step.
+ *
+ * The library is stateless.  The caller (a scheduler) owns every buffer.  The library
+ * never allocates, frees or synchronises; calls are asynchronous on `stream`.
+ *
+ * Common conventions
+ *   - All array pointers are DEVICE pointers on the current HIP device, C-contiguous.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - Element type `dtype`: PKV_F32 (float) or PKV_BF16 (bfloat16 stored as 16 bits).
+ *     q, k/v pools, new K/V and `out` all use the same element type.
+ *   - Pool layout, both pools: [num_blocks][num_kv_heads][16][head_dim].  Each
+ *     (block, kv-head) tile is one contiguous run of 16*head_dim elements.
+ *   - Flat slot s names pool position (block s / 16, offset s % 16).
+ *   - Supported shapes: block_size == 16, head_dim in {64, 128},
+ *     num_q_heads % num_kv_heads == 0.  Anything else is PKV_ERR_UNSUPPORTED or
+ *     PKV_ERR_INVALID_ARG, returned before any launch.
+ *   - Device-resident metadata (slots, table entries, lengths) are trusted
+ *     preconditions.  Kernels never access memory outside the buffers whatever their
+ *     values, but results for invalid metadata are unspecified;
+ *     pkv_validate_metadata() checks host copies.
+ *   - No exception crosses the ABI.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes   */
+  PKV_ERR_UNSUPPORTED = 2, /* block_size != 16, head_dim not 64/128, bad dtype   */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required         */
+  PKV_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch        */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+#define PKV_BLOCK_SIZE 16
+
+/*
+ * paged_kv_write -- store this step's new K/V rows into their pool slots.
+ * (Serving-engine KV page, section 2, "blocks and block table"; the inference-engine
+ * page's KV-cache section: only the new tokens' K/V are produced each step.)
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim]           (read)
+ *   k_pool, v_pool [num_blocks][num_kv_heads][16][head_dim]       (written)
+ *   slot_mapping   int32 [num_tokens]; token t goes to flat slot slot_mapping[t];
+ *                  a negative slot (or one >= num_blocks*16) skips the token.
+ * Each copied row is a bit-exact copy.  Only the named slots change.  Two tokens
+ * naming the same slot is a precondition violation (either may win).
+ * num_tokens == 0 is a no-op.
+ */
+pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
+                          void *v_pool, const int32_t *slot_mapping, int32_t num_tokens,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, pkv_dtype dtype, void *stream);
+
+/*
+ * paged_attention_workspace_size -- bytes of device scratch that
+ * paged_attention_varlen needs for the same arguments (0 is possible).  The split-K
+ * partial results of long contexts live there.  The host-side shape arguments must
+ * match the later call exactly.
+ */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      pkv_dtype dtype);
+
+/*
+ * paged_attention_varlen -- softmax attention of a varlen batch of query rows over
+ * their sequences' paged K/V (run after paged_kv_write of the same step).
+ * (Serving-engine KV page, section 2: the kernel walks the block table and must equal
+ * attention over a contiguous cache; block sharing; inference-engine page, Chunked
+ * Prefill: prefill slices and decode tokens share one step.)
+ *
+ *   out             [total_q][num_q_heads][head_dim]          (written)
+ *   q               [total_q][num_q_heads][head_dim]
+ *   k_pool, v_pool  [num_blocks][num_kv_heads][16][head_dim]
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]; entry lb of row s is the
+ *                   physical block of sequence s's logical block lb; only entries
+ *                   lb < ceil(context_lens[s]/16) are read
+ *   context_lens    int32 [num_seqs]; keys of sequence s, this step's tokens included
+ *   query_start_loc int32 [num_seqs+1]; rows of sequence s are
+ *                   [query_start_loc[s], query_start_loc[s+1]); query_start_loc[0]==0
+ *   max_context_len host upper bound of context_lens (sizes the split-K plan)
+ *   max_query_len   host upper bound of the per-sequence query counts
+ *   scale           multiplier of q.k before the softmax (e.g. 1/sqrt(head_dim))
+ *   workspace       device scratch of workspace_bytes >= the size query's answer
+ *
+ * Row i of a sequence with q query rows and c keys sits at position c-q+i and sees
+ * keys 0..c-q+i (a decode token, q == 1, sees all c).  Query head h reads KV head
+ * h / (num_q_heads/num_kv_heads).  Rows whose sequence has q > c get zeros.
+ * Output precision: bf16 inputs -> fp32 accumulation, bf16 output rounded to nearest
+ * even; fp32 inputs -> fp32 throughout.
+ */
+pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *block_tables,
+                                  const int32_t *context_lens,
+                                  const int32_t *query_start_loc, int32_t num_seqs,
+                                  int32_t total_q, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, float scale, pkv_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *pkv_status_string(pkv_status status);
+
+/*
+ * pkv_validate_metadata -- host-side check of HOST copies of the metadata (no device
+ * access).  Returns PKV_OK, or PKV_ERR_INVALID_ARG and, if `bad_index` is non-NULL,
+ * the offending sequence (or token, for slot errors) index.  Checks:
+ * query_start_loc non-decreasing from 0 to total_q; 0 <= q_len <= context_len and
+ * context_len <= max_blocks_per_seq*16 per sequence; table entries in
+ * [0, num_blocks) for every used logical block; slots < num_blocks*16 and no slot
+ * named twice (slot_mapping may be NULL to skip the slot checks).
+ */
+pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *query_start_loc,
+                                 const int32_t *slot_mapping, int32_t num_seqs,
+                                 int32_t total_q, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t *bad_index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,9 @@
+"""Paged-KV attention for MI355X (gfx950): a C-ABI HIP library plus a thin binding.
+
+    from paged_kv_cache_290_amd import kv_write, attention, workspace_size
+
+The shared library is loaded lazily on the first call and must have been built with
+`python -m paged_kv_cache_290_amd.build`.
+"""
+from .ops import BLOCK_SIZE, attention, kv_write, validate_metadata, workspace_size  # noqa: F401
+from ._lib import PagedKVError  # noqa: F401

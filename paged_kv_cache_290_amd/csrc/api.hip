@@ -1,0 +1,201 @@
+// extern "C" entry points of libpagedkv: argument checks, the split-K plan and the
+// kernel launches on the caller's stream.  The library is stateless: it allocates
+// nothing, frees nothing and never synchronises.
+#include <math.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <unordered_set>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+int env_int(const char *name, int fallback) {
+  const char *s = getenv(name);
+  if (!s || !*s) return fallback;
+  char *end = nullptr;
+  const long v = strtol(s, &end, 10);
+  return (end && *end == 0 && v > 0 && v < (1 << 20)) ? (int)v : fallback;
+}
+
+bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Query heads per decode workgroup: the largest of 4, 2, 1 dividing the group whose
+// query fragment stays within 512 bytes per lane quarter (keeps registers in check).
+int pick_head_group(int group, int head_dim, pkv_dtype dtype) {
+  const int elem = dtype == PKV_F32 ? 4 : 2;
+  for (int hg = 4; hg > 1; hg >>= 1)
+    if (group % hg == 0 && hg * head_dim * elem <= 512) return hg;
+  return 1;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+                       int head_dim, int max_context_len, pkv_dtype dtype) {
+  DecodePlan p{};
+  p.group = num_q_heads / num_kv_heads;
+  p.head_group = pick_head_group(p.group, head_dim, dtype);
+  p.num_head_groups = p.group / p.head_group;
+  p.items = dtype == PKV_F32 ? total_q : num_seqs;
+  const int nblk = std::max(1, (max_context_len + kBlock - 1) / kBlock);
+  // Blocks per split: a multiple of the 4 waves, at most 256 (64 per wave).  The
+  // default of 16 keeps 4 blocks per wave per split; very long contexts grow the
+  // split so that a row has at most 64 splits.  PKV_DECODE_BLOCKS_PER_SPLIT
+  // overrides it (for tuning sweeps).
+  int bps = env_int("PKV_DECODE_BLOCKS_PER_SPLIT", 16);
+  if (nblk > 64 * bps) bps = (nblk + 63) / 64;
+  bps = std::min(256, std::max(kWaves, (bps + kWaves - 1) / kWaves * kWaves));
+  p.blocks_per_split = bps;
+  p.num_splits = (nblk + bps - 1) / bps;
+  p.ws_o_offset = 0;
+  p.ws_lse_offset = 0;
+  p.ws_bytes = 0;
+  if (p.num_splits > 1 && p.items > 0) {
+    const size_t slots = (size_t)p.items * num_q_heads * p.num_splits;
+    p.ws_lse_offset = align256(slots * head_dim * sizeof(float));
+    p.ws_bytes = p.ws_lse_offset + align256(slots * sizeof(float));
+  }
+  return p;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char *pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                          const int32_t *slot_mapping, int32_t num_tokens,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, pkv_dtype dtype, void *stream) {
+  if (!dtype_ok(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  const hipError_t e = launch_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping,
+                                       num_tokens, num_blocks, num_kv_heads, head_dim, dtype,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, pkv_dtype dtype) {
+  if (num_seqs <= 0 || total_q <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype) ||
+      max_context_len < 0)
+    return 0;
+  return plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                     max_context_len, dtype)
+      .ws_bytes;
+}
+
+pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *block_tables,
+                                  const int32_t *context_lens,
+                                  const int32_t *query_start_loc, int32_t num_seqs,
+                                  int32_t total_q, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, float scale, pkv_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dtype_ok(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || num_blocks <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_context_len < 0 ||
+      max_query_len < 0 || !isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens ||
+      !query_start_loc)
+    return PKV_ERR_INVALID_ARG;
+
+  const DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads,
+                                      head_dim, max_context_len, dtype);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return PKV_ERR_WORKSPACE;
+
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_o_offset);
+  a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_lse_offset);
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_decode(a, plan, dtype, st);
+  if (e == hipSuccess && dtype == PKV_BF16 && max_query_len > 1) e = launch_prefill(a, dtype, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *query_start_loc, const int32_t *slot_mapping,
+                                 int32_t num_seqs, int32_t total_q, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t *bad_index) {
+  auto fail = [&](int idx) {
+    if (bad_index) *bad_index = idx;
+    return PKV_ERR_INVALID_ARG;
+  };
+  if (bad_index) *bad_index = -1;
+  if (num_seqs < 0 || total_q < 0 || num_blocks <= 0 || max_blocks_per_seq < 0)
+    return fail(-1);
+  if (num_seqs > 0 && (!block_tables || !context_lens || !query_start_loc)) return fail(-1);
+  if (num_seqs > 0 && query_start_loc[0] != 0) return fail(0);
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = query_start_loc[s + 1] - query_start_loc[s];
+    const int ctx = context_lens[s];
+    if (q_len < 0 || q_len > ctx) return fail(s);
+    if ((int64_t)ctx > (int64_t)max_blocks_per_seq * kBlock) return fail(s);
+    const int used = (ctx + kBlock - 1) / kBlock;
+    for (int lb = 0; lb < used; ++lb) {
+      const int pb = block_tables[(size_t)s * max_blocks_per_seq + lb];
+      if (pb < 0 || pb >= num_blocks) return fail(s);
+    }
+  }
+  if (num_seqs > 0 && query_start_loc[num_seqs] != total_q) return fail(num_seqs);
+  if (slot_mapping) {
+    std::unordered_set<int64_t> seen;
+    seen.reserve((size_t)total_q * 2);
+    for (int t = 0; t < total_q; ++t) {
+      const int64_t s = slot_mapping[t];
+      if (s < 0) continue;
+      if (s >= (int64_t)num_blocks * kBlock || !seen.insert(s).second) return fail(t);
+    }
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

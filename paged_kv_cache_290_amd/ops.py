@@ -1,0 +1,135 @@
+"""Torch-facing binding of libpagedkv: checks tensor shapes, dtypes and devices, then
+passes raw device pointers and the current HIP stream to the C ABI.  Every step of the
+computation runs in the library's HIP kernels; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+BLOCK_SIZE = 16
+_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype}; use float32 or bfloat16")
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(name: str, t: torch.Tensor, device) -> None:
+    _require(t.is_cuda, f"{name} must be a GPU tensor")
+    _require(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def kv_write(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+             v_pool: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Write new K/V rows [T, Hkv, D] into pools [num_blocks, Hkv, 16, D] at slots."""
+    dev = k_pool.device
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool),
+                 ("slot_mapping", slot_mapping)):
+        _on_gpu(n, t, dev)
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    nb, hkv, bs, d = k_pool.shape
+    _require(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new shape mismatch")
+    _require(tuple(k_new.shape[1:]) == (hkv, d), "new K/V heads or head_dim differ from pool")
+    _require(k_new.dtype == k_pool.dtype == v_new.dtype == v_pool.dtype, "dtype mismatch")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (k_new.shape[0],),
+             "slot_mapping must be int32 [num_tokens]")
+    lib = _lib.load()
+    st = lib.paged_kv_write(k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(),
+                            v_pool.data_ptr(), slot_mapping.data_ptr(), k_new.shape[0], nb,
+                            hkv, d, bs, _dtype_code(k_pool), _stream_handle(stream))
+    _lib.check("paged_kv_write", st)
+
+
+def workspace_size(num_seqs: int, total_q: int, num_q_heads: int, num_kv_heads: int,
+                   head_dim: int, max_context_len: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().paged_attention_workspace_size(
+        num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_context_len,
+        _DTYPES[dtype]))
+
+
+def attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor,
+              query_start_loc: torch.Tensor, *, scale: float, max_context_len: int,
+              max_query_len: int, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Varlen paged attention; returns `out` [total_q, Hq, D] (same dtype as q).
+
+    `max_context_len` / `max_query_len` are host-side upper bounds of the device
+    metadata.  `workspace` (uint8) must hold at least workspace_size(...) bytes; when
+    omitted it is allocated here.
+    """
+    dev = q.device
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start_loc", query_start_loc)):
+        _on_gpu(n, t, dev)
+    _require(q.dim() == 3, "q must be [total_q, Hq, D]")
+    total_q, hq, d = q.shape
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    nb, hkv, bs, d2 = k_pool.shape
+    _require(d2 == d, "head_dim of q and pools differ")
+    _require(q.dtype == k_pool.dtype == v_pool.dtype, "dtype mismatch")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2,
+             "block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    num_seqs, max_blocks = block_tables.shape
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (num_seqs,),
+             "context_lens must be int32 [num_seqs]")
+    _require(query_start_loc.dtype == torch.int32 and
+             query_start_loc.shape == (num_seqs + 1,),
+             "query_start_loc must be int32 [num_seqs + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _on_gpu("out", out, dev)
+        _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    need = workspace_size(num_seqs, total_q, hq, hkv, d, max_context_len, q.dtype) \
+        if num_seqs and total_q else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _on_gpu("workspace", workspace, dev)
+    lib = _lib.load()
+    st = lib.paged_attention_varlen(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(),
+        num_seqs, total_q, nb, max_blocks, max_context_len, max_query_len, hq, hkv, d, bs,
+        float(scale), _dtype_code(q), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check("paged_attention_varlen", st)
+    return out
+
+
+def validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
+                      num_blocks: int) -> tuple[bool, int]:
+    """Host-side metadata check on CPU int32 arrays/tensors; (ok, bad_index)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc, dtype=np.int32))
+    sm = None if slot_mapping is None else \
+        np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int32))
+    bad = ctypes.c_int32(-1)
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+    st = _lib.load().pkv_validate_metadata(
+        ptr(bt), ptr(cl), ptr(qsl), ptr(sm), cl.shape[0], int(qsl[-1]) if qsl.size else 0,
+        num_blocks, bt.shape[1] if bt.ndim == 2 else 0, ctypes.byref(bad))
+    return st == _lib.PKV_OK, bad.value
