@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: the slot write of the step's new
+K/V (paged_kv_write) followed by varlen paged attention (paged_attention_varlen).
+
+Default workload (the one the headline metric is quoted on): Llama-3.2-1B-shaped
+single-layer decode in bf16, 32 sequences, 32 query / 8 KV heads, head_dim 64,
+16-token blocks, contexts uniform in [128, 2048], a pool of 8,192 blocks.
+
+Timing
+  * Inputs are resident in HBM before timing starts.  R device copies of the batch
+    (separate pools, tables, queries) are used round-robin, with R chosen so that R
+    working sets exceed 1 GiB, four times the 256 MB MALL: each step's K/V comes from
+    HBM, not from the last-level cache.
+  * W eager warm-up steps run first.  Then exactly K steps are captured into one HIP
+    graph; after one untimed warm replay, the timed replay is bracketed by
+    torch.cuda.synchronize() on both sides (one process, one GPU: no barrier needed).
+  * The attention call's average duration (`roofline.achieved`) is timed separately
+    with HIP events on the launch stream, in an eager loop queued behind a spin kernel
+    so the GPU runs the calls back to back.
+  * value = algorithmic bytes of one step / ms_per_step (GB/s).  Algorithmic bytes
+    count every logical KV token of a sequence once (shared-prefix blocks once per
+    physical block), plus q, out, table entries, lengths, and the write's new K/V
+    read and stored, and its slot indices.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                       [--only-main]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "paged-attn decode KV GB/s (% of HBM peak); prefill-chunk TFLOP/s (% MFMA)"
+MAIN = "llama32_1b_decode"
+ROTATE_BYTES = 1 << 30
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (counts only; no attention arithmetic)
+# ---------------------------------------------------------------------------
+
+def kv_token_slots(b) -> int:
+    """Distinct pool slots the attention reads (shared blocks count once)."""
+    import numpy as np
+
+    seen = {}
+    for s in range(b.num_seqs):
+        c = int(b.context_lens[s])
+        nb = (c + 15) // 16
+        for lb in range(nb):
+            pb = int(b.block_tables[s, lb])
+            used = min(16, c - lb * 16)
+            seen[pb] = max(seen.get(pb, 0), used)
+    del np
+    return sum(seen.values())
+
+
+def attention_bytes(b, unique=True) -> int:
+    e = b.elem_bytes
+    toks = kv_token_slots(b) if unique else int(b.context_lens.sum())
+    kv = toks * b.num_kv_heads * b.head_dim * e * 2
+    qo = 2 * b.total_q * b.num_q_heads * b.head_dim * e
+    meta = int(((b.context_lens.astype("int64") + 15) // 16).sum()) * 4
+    meta += 4 * b.num_seqs + 4 * (b.num_seqs + 1)
+    return kv + qo + meta
+
+
+def write_bytes(b) -> int:
+    return 2 * 2 * b.total_q * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.total_q
+
+
+def chunk_flops(b) -> int:
+    """4 * D * Hq per attended (query, key) pair of the rows with q_len > 1."""
+    pairs = 0
+    for s in range(b.num_seqs):
+        q = int(b.query_lens[s])
+        if q > 1:
+            c = int(b.context_lens[s])
+            pairs += sum(c - q + i + 1 for i in range(q))
+    return 4 * b.head_dim * b.num_q_heads * pairs
+
+
+# ---------------------------------------------------------------------------
+# device side
+# ---------------------------------------------------------------------------
+
+class Runner:
+    """R device copies of one batch and the step on copy i % R."""
+
+    def __init__(self, b, rotate: int):
+        import torch
+        from tests.gpu_util import DeviceBatch
+        import paged_kv_cache_290_amd as pkv
+
+        self.b, self.pkv, self.torch = b, pkv, torch
+        base = DeviceBatch(b)
+        self.sets = [base]
+        for _ in range(rotate - 1):
+            c = DeviceBatch.__new__(DeviceBatch)
+            c.b = b
+            for f in ("k_pool", "v_pool", "q", "k_new", "v_new", "block_tables",
+                      "context_lens", "query_start_loc", "slot_mapping"):
+                setattr(c, f, getattr(base, f).clone())
+            self.sets.append(c)
+        for s in self.sets:
+            s.out = torch.empty_like(s.q)
+        nbytes = pkv.workspace_size(b.num_seqs, b.total_q, b.num_q_heads, b.num_kv_heads,
+                                    b.head_dim, b.max_context_len, base.q.dtype)
+        self.ws = [torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+                   for _ in self.sets]
+
+    def write(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.pkv.kv_write(s.k_new, s.v_new, s.k_pool, s.v_pool, s.slot_mapping)
+
+    def attend(self, i):
+        s = self.sets[i % len(self.sets)]
+        b = self.b
+        self.pkv.attention(s.q, s.k_pool, s.v_pool, s.block_tables, s.context_lens,
+                           s.query_start_loc, scale=b.scale,
+                           max_context_len=b.max_context_len,
+                           max_query_len=b.max_query_len, out=s.out,
+                           workspace=self.ws[i % len(self.sets)])
+
+    def step(self, i):
+        self.write(i)
+        self.attend(i)
+
+
+def time_graph(r: Runner, steps: int, warmup: int, write=True) -> float:
+    """ms per step from one HIP graph of exactly `steps` steps."""
+    torch = r.torch
+    fn = r.step if write else r.attend
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()                         # untimed warm replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_calls(r: Runner, calls: int, write_between=True) -> float:
+    """Average duration (ms) of the attention call, from HIP events on its stream."""
+    torch = r.torch
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i in range(2):
+        r.step(i)
+    torch.cuda.synchronize()
+    # queue everything behind a spin kernel so the calls run back to back on the GPU
+    torch.cuda._sleep(int(2e8))
+    for i in range(calls):
+        if write_between:
+            r.write(i)
+        evs[i][0].record(stream)
+        r.attend(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / calls
+
+
+def rotation_for(b) -> int:
+    per = attention_bytes(b) + write_bytes(b)
+    return max(2, min(32, math.ceil(ROTATE_BYTES / per)))
+
+
+# ---------------------------------------------------------------------------
+# oracle timing (CPU baseline leg)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(b, budget_s: float = 10.0) -> dict:
+    """The CPU oracle (as is) on the main workload: slot write + paged attention,
+    repeated whole steps until about `budget_s` seconds have run."""
+    from threadpoolctl import threadpool_info
+    import oracle.pagedkv_oracle as O
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.step(b)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    per_step = el / reps
+    gbs = (attention_bytes(b) + write_bytes(b)) / per_step / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} whole steps of {b.name} (seed 0), fp64 NumPy, "
+                      f"{per_step * 1e3:.1f} ms per step",
+            "host_cpus": os.cpu_count()}
+
+
+# ---------------------------------------------------------------------------
+# counters taken offline (profiles/traffic.json), valid only for unchanged kernels
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_290_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    ent = t.get("workloads", {}).get(workload)
+    return None if ent is None else ent.get("bytes_per_call")
+
+
+# ---------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true",
+                    help="skip the other four workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
+              "part of it (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- the headline workload ----
+    log(f"generating {MAIN}")
+    b = make_config(MAIN, 0)
+    rot = rotation_for(b)
+    r = Runner(b, rot)
+    log(f"timing {args.steps} graph-captured steps over {rot} rotating copies")
+    ms = time_graph(r, args.steps, args.warmup)
+    attn_ms = time_calls(r, args.steps)
+    abytes, wbytes = attention_bytes(b), write_bytes(b)
+    value = (abytes + wbytes) / (ms * 1e-3) / 1e9
+    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(MAIN),
+            "kernel": "paged_attention_varlen (decode_splitk_kernel + merge_kernel)",
+            "algorithmic_bytes": abytes, "avg_ms": round(attn_ms, 5)}
+    del r
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": MAIN, "batch": 32, "num_q_heads": 32, "num_kv_heads": 8,
+                   "head_dim": 64, "block_size": 16, "context_lens": "U[128,2048]",
+                   "pool_blocks": 8192, "seed": 0, "rotating_copies": rot,
+                   "timed_region": "HIP graph of the K steps"},
+        "roofline": roof,
+    }
+
+    # ---- the other workloads (context lines, same protocol) ----
+    if not args.only_main:
+        extra = {}
+        for name in ("qwen3_1p7b_decode_640", "shared_prefix_decode",
+                     "chunked_prefill_mixed", "tiny_f32_decode"):
+            log(f"generating {name}")
+            bx = make_config(name, 0)
+            rx = Runner(bx, rotation_for(bx))
+            msx = time_graph(rx, args.steps, args.warmup)
+            ax = time_calls(rx, args.steps)
+            ab, wb = attention_bytes(bx), write_bytes(bx)
+            ent = {"ms_per_step": round(msx, 5), "attn_ms": round(ax, 5),
+                   "step_GBs": round((ab + wb) / (msx * 1e-3) / 1e9, 1),
+                   "attn_GBs": round(ab / (ax * 1e-3) / 1e9, 1),
+                   "attn_hbm_frac": round(ab / (ax * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if name == "shared_prefix_decode":
+                lb = attention_bytes(bx, unique=False)
+                ent["attn_logical_GBs"] = round(lb / (ax * 1e-3) / 1e9, 1)
+            if name == "chunked_prefill_mixed":
+                fl = chunk_flops(bx)
+                ent["step_TFLOPs"] = round(fl / (msx * 1e-3) / 1e12, 2)
+                del rx
+                torch.cuda.empty_cache()
+                # the chunk alone: sequence 0 only
+                from workloads.synth import PagedBatch  # noqa: F401
+                import copy
+                bc = copy.copy(bx)
+                bc.block_tables = bx.block_tables[:1]
+                bc.context_lens = bx.context_lens[:1]
+                q0 = int(bx.query_start_loc[1])
+                bc.query_start_loc = bx.query_start_loc[:2]
+                bc.q, bc.k_new, bc.v_new = bx.q[:q0], bx.k_new[:q0], bx.v_new[:q0]
+                bc.slot_mapping = bx.slot_mapping[:q0]
+                rc = Runner(bc, 4)
+                cms = time_calls(rc, args.steps, write_between=False)
+                cfl = chunk_flops(bc)
+                tfs = cfl / (cms * 1e-3) / 1e12
+                result["prefill_chunk"] = {
+                    "workload": "chunked_prefill_mixed: the 2,017-row chunk alone",
+                    "bound": "mfma", "achieved": round(tfs, 2),
+                    "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                    "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4), "flops": cfl,
+                    "avg_ms": round(cms, 5), "kernel": "prefill_mfma_kernel"}
+                del rc
+            else:
+                del rx
+            torch.cuda.empty_cache()
+            extra[name] = ent
+        result["workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

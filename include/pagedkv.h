@@ -75,9 +75,10 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
 
 /*
  * paged_attention_workspace_size -- bytes of device scratch that
- * paged_attention_varlen needs for the same arguments (0 is possible).  The split-K
- * partial results of long contexts live there.  The host-side shape arguments must
- * match the later call exactly.
+ * paged_attention_varlen needs for the same arguments on the current device (0 only
+ * for an empty batch or invalid shapes).  It holds the split-K partial results and a
+ * small descriptor per (row, kv-head group); its size depends on the
+ * device's compute-unit count.  The shape arguments must match the later call.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,
                                       int32_t num_q_heads, int32_t num_kv_heads,
@@ -104,6 +105,8 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,
  *   max_query_len   host upper bound of the per-sequence query counts
  *   scale           multiplier of q.k before the softmax (e.g. 1/sqrt(head_dim))
  *   workspace       device scratch of workspace_bytes >= the size query's answer
+ *                   (contents need no initialisation); calls that overlap in time
+ *                   need separate workspaces.
  *
  * Row i of a sequence with q query rows and c keys sits at position c-q+i and sees
  * keys 0..c-q+i (a decode token, q == 1, sees all c).  Query head h reads KV head

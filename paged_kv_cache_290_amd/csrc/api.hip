@@ -18,7 +18,7 @@ int env_int(const char *name, int fallback) {
   if (!s || !*s) return fallback;
   char *end = nullptr;
   const long v = strtol(s, &end, 10);
-  return (end && *end == 0 && v > 0 && v < (1 << 20)) ? (int)v : fallback;
+  return (end && *end == 0 && v >= 0 && v < (1 << 20)) ? (int)v : fallback;
 }
 
 bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
@@ -36,31 +36,41 @@ int pick_head_group(int group, int head_dim, pkv_dtype dtype) {
 
 }  // namespace
 
+// Compute units of the current device (256 on MI355X; also the answer when no device
+// is visible, so host-only size queries agree with the GPU).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
                        int head_dim, int max_context_len, pkv_dtype dtype) {
+  (void)max_context_len;
   DecodePlan p{};
   p.group = num_q_heads / num_kv_heads;
   p.head_group = pick_head_group(p.group, head_dim, dtype);
   p.num_head_groups = p.group / p.head_group;
   p.items = dtype == PKV_F32 ? total_q : num_seqs;
-  const int nblk = std::max(1, (max_context_len + kBlock - 1) / kBlock);
-  // Blocks per split: a multiple of the 4 waves, at most 256 (64 per wave).  The
-  // default of 16 keeps 4 blocks per wave per split; very long contexts grow the
-  // split so that a row has at most 64 splits.  PKV_DECODE_BLOCKS_PER_SPLIT
-  // overrides it (for tuning sweeps).
-  int bps = env_int("PKV_DECODE_BLOCKS_PER_SPLIT", 16);
-  if (nblk > 64 * bps) bps = (nblk + 63) / 64;
-  bps = std::min(256, std::max(kWaves, (bps + kWaves - 1) / kWaves * kWaves));
-  p.blocks_per_split = bps;
-  p.num_splits = (nblk + bps - 1) / bps;
+  // PKV_DECODE_PREFETCH and PKV_DECODE_WGS_PER_CU override the defaults (tuning).
+  int prefetch = env_int("PKV_DECODE_PREFETCH", 1);
+  p.prefetch = (prefetch == 2) ? 2 : 1;
+  int per_cu = env_int("PKV_DECODE_WGS_PER_CU", 2);
+  per_cu = std::max(1, std::min(8, per_cu));
+  p.grid = device_cus() * per_cu;
+  const int chunk = std::min(p.items, kMaxStreamItems);
+  const size_t slots = (size_t)chunk * num_kv_heads * p.num_head_groups +
+                       (size_t)p.grid * kWaves;
   p.ws_o_offset = 0;
-  p.ws_lse_offset = 0;
-  p.ws_bytes = 0;
-  if (p.num_splits > 1 && p.items > 0) {
-    const size_t slots = (size_t)p.items * num_q_heads * p.num_splits;
-    p.ws_lse_offset = align256(slots * head_dim * sizeof(float));
-    p.ws_bytes = p.ws_lse_offset + align256(slots * sizeof(float));
-  }
+  p.ws_lse_offset = align256(slots * p.head_group * head_dim * sizeof(float));
+  p.ws_seginfo_offset = p.ws_lse_offset + align256(slots * p.head_group * sizeof(float));
+  const size_t segments = (size_t)chunk * num_kv_heads * p.num_head_groups;
+  p.ws_bytes = p.items > 0 ? p.ws_seginfo_offset + align256(segments * 2 * sizeof(int)) : 0;
   return p;
 }
 
@@ -130,10 +140,11 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
       !query_start_loc)
     return PKV_ERR_INVALID_ARG;
 
-  const DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads,
-                                      head_dim, max_context_len, dtype);
+  DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                max_context_len, dtype);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return PKV_ERR_WORKSPACE;
+  plan.workspace = workspace;
 
   AttnArgs a{};
   a.out = out;
@@ -143,8 +154,6 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.query_start_loc = query_start_loc;
-  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_o_offset);
-  a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_lse_offset);
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.num_blocks = num_blocks;
@@ -156,8 +165,13 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_decode(a, plan, dtype, st);
-  if (e == hipSuccess && dtype == PKV_BF16 && max_query_len > 1) e = launch_prefill(a, dtype, st);
+  // bf16 rows of chunks (q_len >= 2) go to the MFMA kernel, all other rows to the
+  // decode kernel.  A single sequence with several rows has no decode row.
+  const bool chunks = dtype == PKV_BF16 && max_query_len > 1;
+  const bool decode_rows = !(chunks && num_seqs == 1 && total_q > 1);
+  hipError_t e = hipSuccess;
+  if (decode_rows) e = launch_decode(a, plan, dtype, st);
+  if (e == hipSuccess && chunks) e = launch_prefill(a, dtype, st);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

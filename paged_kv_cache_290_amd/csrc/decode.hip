@@ -1,4 +1,5 @@
-// Decode attention over the paged KV pool: split-K over the context, then a merge.
+// Decode attention over the paged KV pool: balanced split-K (stream-K) over the
+// context, then a log-sum-exp merge.
 //
 // Method (pages cited by title and section):
 //  * Inference-engine page (xiaohu-jiedu), prefill/decode section: a decode step has
@@ -8,21 +9,25 @@
 //    16-token blocks anywhere in the pool; the kernel follows the request's block
 //    table and must give the same result as a contiguous cache.
 //
-// Work item = (row, kv head, group of HG q heads, split of `bps` logical blocks).
-// One workgroup of 4 waves per item; wave w takes blocks w, w+4, ... of the split.
-// Lane mapping inside a wave, for one (block, kv head) tile of 16 x D elements:
-// lane = 4*token + quarter, so a lane owns D/4 consecutive dims of one token, and a
-// wave reads the whole contiguous tile (2-8 KB) with 16-byte loads.  Each K/V tile
-// is loaded once and used for all HG query heads (grouped-query reuse).
+// Work decomposition.  A segment is (kv-head group g, row): the blocks one row must
+// read for the HG query heads of group g.  All segments, concatenated in (g, row,
+// block) order, form one sequence of T blocks.  The grid is persistent (a fixed
+// number of workgroups per CU) and wave w of the W waves takes the contiguous range
+// [w*T/W, (w+1)*T/W), so every wave streams the same number of blocks whatever the
+// context lengths.  A segment that lies inside one wave is finished there; a segment
+// cut across waves leaves one normalised partial (o, log2-sum-exp) per piece, in
+// workspace slot (segment + wave), and the merge kernel combines them.  Slots of
+// different segments never collide: segment s+1 starts at or after the last wave of
+// segment s, so its slots start past segment s's.
 //
-// Softmax runs in log2 units (scores times scale*log2 e, exp2).  Every lane keeps
-// its own running sum and accumulator for its token slot, all scaled by one
-// wave-uniform reference max per head.  The reference is raised only when some
-// score exceeds it by more than kRescaleSlack (then every lane rescales), so the
-// usual per-block cross-lane max is replaced by one ballot.  Terms are at most
-// 2^kRescaleSlack, far from fp32 overflow for any context length in int32.
-// The lanes' partial sums are combined once at the end (DPP inside rows of 16 lanes,
-// then LDS across rows and waves).
+// Per block a wave reads one contiguous (block, kv head) tile of K and of V (2-8 KB
+// each) with 16-byte-per-lane raw buffer loads and uses it for all HG query heads
+// (grouped-query reuse), keeping PF blocks in flight in a register ring while it
+// computes one.  Softmax runs in log2 units (scores times scale*log2 e, exp2).  Every
+// lane keeps running sums for its own tokens, all scaled by one wave-uniform reference
+// max per head; the reference is raised only when some score exceeds it by more than
+// kRescaleSlack (then every lane rescales), so the usual per-block cross-lane max is
+// replaced by one ballot.  Terms stay below 2^kRescaleSlack, far from fp32 overflow.
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -32,329 +37,456 @@ namespace pkv {
 
 constexpr float kRescaleSlack = 8.0f;
 
+// Lane mapping for one (block, kv head) tile of 16 tokens x D elements, row R bytes.
+// Load instruction j of a wave reads the tile's j-th contiguous KiB: lane l gets the
+// 16 bytes at 1024*j + 16*l, i.e. chunk c = l % CPR (EPC elements) of token
+// TPI*j + l / CPR.  A lane thus owns the same EPC dims of NV tokens, and each token's
+// dot product is summed over its CPR lanes.
 template <typename T, int D>
-struct DecodeFrag {
-  static constexpr int kDimsPerLane = D / 4;
-  static constexpr int kVecs = kDimsPerLane * (int)sizeof(T) / 16;  // uint4 per lane
-  static constexpr int kWords = kVecs * 4;                          // dwords per lane
+struct DecodeMap {
+  static constexpr int R = D * (int)sizeof(T);  // bytes per token row
+  static constexpr int CPR = R / 16;            // lanes (16-byte chunks) per token
+  static constexpr int TPI = 64 / CPR;          // tokens per load instruction
+  static constexpr int NV = 16 / TPI;           // load instructions per tile
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  static constexpr int WPC = 4;                 // dwords per chunk
 };
 
-// Row handled by work item `item`, and how many keys it sees (0 when the sequence
-// breaks q_len <= context_len).  Returns false when the item is not a decode row.
+// Sum over the CPR lanes of a token (lanes l with equal l / CPR).
+template <int CPR>
+__device__ __forceinline__ float sum_over_token_lanes(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  if constexpr (CPR >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (CPR >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (CPR >= 32) x += shfl_xor(x, 16);
+  return x;
+}
+
+// Sum over the lanes that own the same chunk (l % CPR equal), i.e. across tokens.
+template <int CPR>
+__device__ __forceinline__ float sum_over_chunk_lanes(float x) {
+  if constexpr (CPR <= 8) x += dpp<kRowRor8>(x);
+  if constexpr (CPR <= 16) x += shfl_xor(x, 16);
+  x += shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  x = fmaxf(x, shfl_xor(x, 16));
+  x = fmaxf(x, shfl_xor(x, 32));
+  return x;
+}
+
+// Row geometry of work item `item`: the query row, its sequence, and how many keys it
+// sees.  Items are sequences for bf16 (only single-query sequences are decode rows;
+// chunks go to the MFMA kernel) and query rows for fp32.  `zero` marks rows that break
+// q_len <= context_len, whose output is defined as zeros.
 template <bool kRows>
-__device__ __forceinline__ bool decode_row(const AttnArgs &a, int item, int &seq, int &row,
-                                           int &row_keys) {
+__device__ __forceinline__ bool item_row(const AttnArgs &a, int item, int &seq, int &row,
+                                         int &keys, bool &zero) {
   if constexpr (kRows) {
     row = item;
     seq = find_seq(a.query_start_loc, a.num_seqs, row);
   } else {
     seq = item;
     row = a.query_start_loc[seq];
-    if (a.query_start_loc[seq + 1] - row != 1) return false;  // prefill: MFMA path
-    if (row < 0 || row >= a.total_q) return false;
+    if (a.query_start_loc[seq + 1] - row != 1 || row < 0 || row >= a.total_q) return false;
   }
   const int q_begin = a.query_start_loc[seq];
   const int q_len = a.query_start_loc[seq + 1] - q_begin;
   const int ctx = a.context_lens[seq];
-  row_keys = ctx - q_len + (row - q_begin) + 1;
-  row_keys = min(row_keys, a.max_blocks_per_seq * kBlock);
-  if (ctx < q_len) row_keys = 0;
+  zero = ctx < q_len;
+  keys = zero ? 0 : min(ctx - q_len + (row - q_begin) + 1, a.max_blocks_per_seq * kBlock);
   return true;
 }
 
-template <typename T, int D, int HG>
-__global__ __launch_bounds__(kThreads) void decode_splitk_kernel(AttnArgs a, int items,
-                                                                 int num_head_groups,
-                                                                 int bps, int num_splits) {
-  constexpr bool kF32 = std::is_same<T, float>::value;
-  using Fr = DecodeFrag<T, D>;
-  constexpr int DPL = Fr::kDimsPerLane;
-  constexpr int NV = Fr::kVecs;
-  constexpr int NW = Fr::kWords;
+// Per-item block counts -> exclusive prefix in LDS (s_pref[0..items], s_pref[items] =
+// total), visible keys in s_keys.  Whole workgroup; ends with a barrier.
+template <bool kRows>
+__device__ __forceinline__ void scan_items(const AttnArgs &a, int base, int items,
+                                           int *s_pref, int *s_keys, int *s_tmp) {
+  const int tid = threadIdx.x;
+  const int per = (items + kThreads - 1) / kThreads;
+  const int i0 = min(items, tid * per);
+  const int i1 = min(items, i0 + per);
+  int local = 0;
+  for (int i = i0; i < i1; ++i) {
+    int seq, row, keys;
+    bool zero;
+    if (!item_row<kRows>(a, base + i, seq, row, keys, zero)) keys = 0;
+    s_keys[i] = keys;
+    const int n = (keys + kBlock - 1) / kBlock;
+    s_pref[i] = n;
+    local += n;
+  }
+  s_tmp[tid] = local;
+  __syncthreads();
+  if (tid < 64) {  // exclusive scan of the 256 thread totals by one wave
+    int v0 = s_tmp[4 * tid], v1 = s_tmp[4 * tid + 1], v2 = s_tmp[4 * tid + 2],
+        v3 = s_tmp[4 * tid + 3];
+    const int sum = v0 + v1 + v2 + v3;
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (tid >= d) incl += o;
+    }
+    int ex = incl - sum;
+    s_tmp[4 * tid] = ex; ex += v0;
+    s_tmp[4 * tid + 1] = ex; ex += v1;
+    s_tmp[4 * tid + 2] = ex; ex += v2;
+    s_tmp[4 * tid + 3] = ex; ex += v3;
+    if (tid == 63) s_pref[items] = ex;
+  }
+  __syncthreads();
+  int run = s_tmp[tid];
+  for (int i = i0; i < i1; ++i) {
+    const int n = s_pref[i];
+    s_pref[i] = run;
+    run += n;
+  }
+  __syncthreads();
+}
 
-  __shared__ float s_acc[kWaves][4][HG][D];
-  __shared__ float s_l[kWaves][4][HG];
-  __shared__ float s_m[kWaves][HG];
+template <typename T, int D, int HG, int PF>
+__global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, StreamArgs p) {
+  constexpr bool kF32 = std::is_same<T, float>::value;
+  using M = DecodeMap<T, D>;
+  constexpr int CPR = M::CPR, TPI = M::TPI, NV = M::NV, EPC = M::EPC, WPC = M::WPC;
+  constexpr int kTileBytes = kBlock * D * (int)sizeof(T);
+
+  __shared__ int s_pref[kMaxStreamItems + 1];
+  __shared__ int s_keys[kMaxStreamItems];
+  __shared__ int s_tmp[kThreads];
+
+  scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_tmp);
+  const int rows_total = s_pref[p.items];
+  const int64_t T_all = (int64_t)rows_total * p.groups;
+  // With fewer blocks than waves only the first T_all waves work, so every working
+  // wave owns at least one block.
+  const int W = (int)min<int64_t>((int64_t)gridDim.x * kWaves, T_all);
+  if (blockIdx.x == 0) {
+    // Rows of sequences that break q_len <= context_len: defined as zeros.
+    for (int i = threadIdx.x; i < p.items; i += kThreads) {
+      int seq, row, keys;
+      bool zero;
+      if (item_row<kF32>(a, p.item_base + i, seq, row, keys, zero) && zero)
+        for (int e = 0; e < a.num_q_heads * D; ++e)
+          static_cast<T *>(a.out)[(size_t)row * a.num_q_heads * D + e] = T(0);
+    }
+    // Per segment (g, item): first partial slot and piece count for the merge kernel
+    // (0 pieces: nothing to merge, the segment was finished in one wave or is empty).
+    for (int sg = threadIdx.x; sg < p.items * p.groups; sg += kThreads) {
+      const int g = sg / p.items;
+      const int item = sg - g * p.items;
+      int first = 0, pieces = 0;
+      if (s_pref[item + 1] > s_pref[item]) {
+        const int64_t s0 = (int64_t)g * rows_total + s_pref[item];
+        const int64_t s1 = s0 + (s_pref[item + 1] - s_pref[item]);
+        const int w0 = (int)(((s0 + 1) * W - 1) / T_all);
+        const int w1 = (int)((s1 * W - 1) / T_all);
+        if (w1 > w0) {
+          first = sg + w0;
+          pieces = w1 - w0 + 1;
+        }
+      }
+      p.seginfo[2 * sg] = first;
+      p.seginfo[2 * sg + 1] = pieces;
+    }
+  }
+  if (T_all == 0) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tok = lane >> 2;
-  const int quarter = lane & 3;
-
-  const int total = items * a.num_kv_heads * num_head_groups * num_splits;
-  int v = xcd_remap(blockIdx.x, total);
-  if (v >= total) return;
-  const int item = v % items;
-  v /= items;
-  const int split = v % num_splits;
-  v /= num_splits;
-  const int hgi = v % num_head_groups;
-  const int kvh = v / num_head_groups;
-
-  int seq, row, row_keys;
-  if (!decode_row<kF32>(a, item, seq, row, row_keys)) return;
+  const int chunk = lane % CPR;
+  const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
+  const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
+  if (w >= W) return;
+  int64_t b = (int64_t)w * T_all / W;
+  const int64_t b_end = (int64_t)(w + 1) * T_all / W;
   const int group = a.num_q_heads / a.num_kv_heads;
-  const int h0 = kvh * group + hgi * HG;
-  T *out = static_cast<T *>(a.out);
+  const char *kpool = static_cast<const char *>(a.k_pool);
+  const char *vpool = static_cast<const char *>(a.v_pool);
 
-  if (row_keys <= 0) {  // q_len > context_len: defined as zeros
-    if (split == 0)
-      for (int o = threadIdx.x; o < HG * D; o += kThreads)
-        out[((size_t)row * a.num_q_heads + h0) * D + o] = T(0);
-    return;
-  }
-  // The split plan comes from the host's max_context_len; a longer row is cut there.
-  const int nblk = min((row_keys + kBlock - 1) / kBlock, num_splits * bps);
-  row_keys = min(row_keys, nblk * kBlock);
-  const int row_splits = (nblk + bps - 1) / bps;
-  if (split >= row_splits) return;
-  const int b0 = split * bps;
-  const int b1 = min(nblk, b0 + bps);
-  const int nb_w = (b1 - b0 > wave) ? (b1 - b0 - wave + kWaves - 1) / kWaves : 0;
+  while (b < b_end) {
+    // ---- locate the piece: group g, item, first logical block, block count ----
+    const int g = (int)(b / rows_total);
+    const int r = (int)(b - (int64_t)g * rows_total);
+    int lo = 0, hi = p.items - 1;  // last item with s_pref[item] <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int item = lo;
+    const int lb0 = r - s_pref[item];
+    const int n_item = s_pref[item + 1] - s_pref[item];
+    const int n = (int)min<int64_t>(n_item - lb0, b_end - b);
+    const bool whole = lb0 == 0 && n == n_item;
+    const int seg = g * p.items + item;
+    b += n;
 
-  // Query fragment: this lane's D/4 dims of each of the HG heads.
-  uint32_t qw[HG][NW];
-  {
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
-                  quarter * DPL;
-#pragma unroll
-    for (int g = 0; g < HG; ++g) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(qp + g * D);
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const uint4 x = src[j];
-        qw[g][4 * j + 0] = x.x;
-        qw[g][4 * j + 1] = x.y;
-        qw[g][4 * j + 2] = x.z;
-        qw[g][4 * j + 3] = x.w;
-      }
-      if constexpr (kF32) {  // fold the softmax scale into q once
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-          qw[g][i] = __float_as_uint(__uint_as_float(qw[g][i]) * a.scale_log2);
-      }
-    }
-  }
+    int seq, row, keys;
+    bool zero;
+    item_row<kF32>(a, p.item_base + item, seq, row, keys, zero);
+    const int kvh = g / p.num_head_groups;
+    const int h0 = kvh * group + (g - kvh * p.num_head_groups) * HG;
 
-  // Physical block ids of this wave's blocks: lane i holds the i-th (bps <= 256, so
-  // a wave has at most 64 blocks in a split).
-  int my_pb = 0;
-  {
-    const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
-    if (lane < nb_w) my_pb = tbl[b0 + wave + kWaves * lane];
-  }
-
-  float acc[HG][DPL];
-  float lsum[HG];
-  float mref[HG];
+    // ---- query fragment: this lane's EPC dims (chunk) of each of the HG heads ----
+    uint32_t qw[HG][WPC];
+    {
+      const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
+                    chunk * EPC;
 #pragma unroll
-  for (int g = 0; g < HG; ++g) {
-    lsum[g] = 0.f;
-    mref[g] = -INFINITY;
+      for (int hh = 0; hh < HG; ++hh) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
+        qw[hh][0] = x.x; qw[hh][1] = x.y; qw[hh][2] = x.z; qw[hh][3] = x.w;
+        if constexpr (kF32) {  // fold the softmax scale into q once
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[g][d] = 0.f;
-  }
-
-  const size_t tile_elems = (size_t)kBlock * D;
-  auto tile_base = [&](const void *pool, int pb) {
-    return reinterpret_cast<const uint4 *>(static_cast<const T *>(pool) +
-                                           ((size_t)pb * a.num_kv_heads + kvh) * tile_elems) +
-           lane * NV;
-  };
-  auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
-    int pb = readlane(my_pb, i);
-    pb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
-    const uint4 *kp = tile_base(a.k_pool, pb);
-    const uint4 *vp = tile_base(a.v_pool, pb);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) kr[j] = kp[j];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) vr[j] = vp[j];
-  };
-  auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
-    const int lb = b0 + wave + kWaves * i;
-    const int pb = readlane(my_pb, i);
-    const bool bad = pb < 0 || pb >= a.num_blocks;
-    const bool valid = !bad && (lb * kBlock + tok) < row_keys;
-    uint32_t kw[NW], vw[NW];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      kw[4 * j + 0] = kr[j].x; kw[4 * j + 1] = kr[j].y;
-      kw[4 * j + 2] = kr[j].z; kw[4 * j + 3] = kr[j].w;
-      vw[4 * j + 0] = vr[j].x; vw[4 * j + 1] = vr[j].y;
-      vw[4 * j + 2] = vr[j].z; vw[4 * j + 3] = vr[j].w;
-    }
-    float s[HG];
-#pragma unroll
-    for (int g = 0; g < HG; ++g) {
-      float x = 0.f;
-      if constexpr (kF32) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) x = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kw[w]), x);
-      } else {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) x = dot2_bf16(qw[g][w], kw[w], x);
-      }
-      x += dpp<kQuadSwap1>(x);
-      x += dpp<kQuadSwap2>(x);
-      if constexpr (!kF32) x *= a.scale_log2;
-      s[g] = valid ? x : -INFINITY;
-    }
-    bool need = false;
-#pragma unroll
-    for (int g = 0; g < HG; ++g) need |= s[g] > mref[g] + kRescaleSlack;
-    if (wave_any(need)) {
-#pragma unroll
-      for (int g = 0; g < HG; ++g) {
-        const float mx = wave_max_over_quads(s[g]);
-        const float mn = fmaxf(mref[g], mx);
-        const float alpha = (mref[g] == -INFINITY) ? 0.f : fast_exp2(mref[g] - mn);
-        mref[g] = mn;
-        lsum[g] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[g][d] *= alpha;
-      }
-    }
-    float p[HG];
-#pragma unroll
-    for (int g = 0; g < HG; ++g) {
-      p[g] = valid ? fast_exp2(s[g] - mref[g]) : 0.f;
-      lsum[g] += p[g];
-    }
-    // Slots past the context (and tiles of invalid blocks) may hold anything,
-    // including NaN: their weight is 0 and their values are replaced by 0.
-    if (bad || (lb + 1) * kBlock > row_keys) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) vw[w] = valid ? vw[w] : 0u;
-    }
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if constexpr (kF32) {
-        const float x = __uint_as_float(vw[w]);
-#pragma unroll
-        for (int g = 0; g < HG; ++g) acc[g][w] = fmaf(p[g], x, acc[g][w]);
-      } else {
-        const float lo = bf16_lo(vw[w]);
-        const float hi = bf16_hi(vw[w]);
-#pragma unroll
-        for (int g = 0; g < HG; ++g) {
-          acc[g][2 * w] = fmaf(p[g], lo, acc[g][2 * w]);
-          acc[g][2 * w + 1] = fmaf(p[g], hi, acc[g][2 * w + 1]);
+          for (int k = 0; k < WPC; ++k)
+            qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
         }
       }
     }
-  };
 
-  if (nb_w > 0) {
-    uint4 kA[NV], vA[NV], kB[NV], vB[NV];
-    load(kA, vA, 0);
-    int i = 0;
-    for (; i + 1 < nb_w; i += 2) {
-      load(kB, vB, i + 1);
-      compute(kA, vA, i);
-      if (i + 2 < nb_w) load(kA, vA, i + 2);
-      compute(kB, vB, i + 1);
+    float acc[HG][EPC];
+    float lsum[HG];
+    float mref[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      lsum[hh] = 0.f;
+      mref[hh] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
     }
-    if (i < nb_w) compute(kA, vA, i);
-  }
 
-  // Combine the 4 token slots of each 16-lane row (same quarter = same dims).
-#pragma unroll
-  for (int g = 0; g < HG; ++g) {
-    lsum[g] += dpp<kRowRor4>(lsum[g]);
-    lsum[g] += dpp<kRowRor8>(lsum[g]);
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) {
-      acc[g][d] += dpp<kRowRor4>(acc[g][d]);
-      acc[g][d] += dpp<kRowRor8>(acc[g][d]);
-    }
-  }
-  if ((lane & 15) < 4) {
-    const int r = lane >> 4;
-#pragma unroll
-    for (int g = 0; g < HG; ++g) {
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) s_acc[wave][r][g][quarter * DPL + d] = acc[g][d];
-      if (quarter == 0) s_l[wave][r][g] = lsum[g];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < HG; ++g) s_m[wave][g] = mref[g];
-  }
-  __syncthreads();
+    const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int nc = min(64, n - c0);
+      // Physical block ids of this chunk of the piece: lane i holds the i-th.
+      const int my_pb = lane < nc ? tbl[c0 + lane] : 0;
+      const int lb_first = lb0 + c0;
 
-  for (int o = threadIdx.x; o < HG * D; o += kThreads) {
-    const int g = o / D;
-    const int d = o - g * D;
-    float mx = -INFINITY;
+      // Raw buffer loads through a per-tile descriptor.  Prefetches past the chunk (and
+      // tiles of invalid table entries) get a descriptor with no records: those loads
+      // fetch nothing and return zeros, yet every path issues the same number of
+      // loads, so the compiler's wait counts stay exact.
+      auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
+        int pb = readlane(my_pb, min(i, nc - 1));
+        const bool ok = i < nc && pb >= 0 && pb < a.num_blocks;
+        pb = ok ? pb : 0;
+        const size_t off = ((size_t)pb * a.num_kv_heads + kvh) * kTileBytes;
+        const int nrec = ok ? kTileBytes : 0;
+        const buffer_rsrc_t rk = make_rsrc(kpool + off, nrec);
+        const buffer_rsrc_t rv = make_rsrc(vpool + off, nrec);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][g]);
-    float L = 0.f, O = 0.f;
+        for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - mx);
+        for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
+      };
+      auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
+        const int lb = lb_first + i;
+        const int pb = readlane(my_pb, i);
+        const bool bad = pb < 0 || pb >= a.num_blocks;
+        const int key0 = lb * kBlock + tok0;
+        float s[NV][HG];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        L = fmaf(wt, s_l[w][r][g], L);
-        O = fmaf(wt, s_acc[w][r][g][d], O);
+        for (int j = 0; j < NV; ++j) {
+          const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            float x = 0.f;
+#pragma unroll
+            for (int k = 0; k < WPC; ++k) {
+              if constexpr (kF32)
+                x = fmaf(__uint_as_float(qw[hh][k]), __uint_as_float(kw[k]), x);
+              else
+                x = dot2_bf16(qw[hh][k], kw[k], x);
+            }
+            s[j][hh] = x;
+          }
+        }
+        bool need = false;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const bool valid = !bad && (key0 + TPI * j) < keys;
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            float x = sum_over_token_lanes<CPR>(s[j][hh]);
+            if constexpr (!kF32) x *= a.scale_log2;
+            x = valid ? x : -INFINITY;
+            s[j][hh] = x;
+            need |= x > mref[hh] + kRescaleSlack;
+          }
+        }
+        if (wave_any(need)) {
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            float mx = s[0][hh];
+#pragma unroll
+            for (int j = 1; j < NV; ++j) mx = fmaxf(mx, s[j][hh]);
+            const float mn = fmaxf(mref[hh], wave_max(mx));
+            const float alpha = (mref[hh] == -INFINITY) ? 0.f : fast_exp2(mref[hh] - mn);
+            mref[hh] = mn;
+            lsum[hh] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha;
+          }
+        }
+        // Slots past the context (and tiles of invalid blocks) may hold anything,
+        // including NaN: their weight is 0 and their values are replaced by 0.
+        const bool edge = bad || (lb + 1) * kBlock > keys;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const bool valid = !bad && (key0 + TPI * j) < keys;
+          uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+          if (edge) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vw[k] = valid ? vw[k] : 0u;
+          }
+          float pr[HG];
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            pr[hh] = valid ? fast_exp2(s[j][hh] - mref[hh]) : 0.f;
+            lsum[hh] += pr[hh];
+          }
+#pragma unroll
+          for (int k = 0; k < WPC; ++k) {
+            if constexpr (kF32) {
+              const float x = __uint_as_float(vw[k]);
+#pragma unroll
+              for (int hh = 0; hh < HG; ++hh) acc[hh][k] = fmaf(pr[hh], x, acc[hh][k]);
+            } else {
+              const float lo = bf16_lo(vw[k]);
+              const float hi = bf16_hi(vw[k]);
+#pragma unroll
+              for (int hh = 0; hh < HG; ++hh) {
+                acc[hh][2 * k] = fmaf(pr[hh], lo, acc[hh][2 * k]);
+                acc[hh][2 * k + 1] = fmaf(pr[hh], hi, acc[hh][2 * k + 1]);
+              }
+            }
+          }
+        }
+      };
+
+      // Ring of PF+1 register buffers: while block i is computed, blocks i+1..i+PF
+      // are in flight.
+      uint4 kb[PF + 1][NV], vb[PF + 1][NV];
+#pragma unroll
+      for (int q = 0; q < PF; ++q) load(kb[q], vb[q], q);
+      for (int i0 = 0; i0 < nc; i0 += PF + 1) {
+#pragma unroll
+        for (int u = 0; u <= PF; ++u) {
+          load(kb[(u + PF) % (PF + 1)], vb[(u + PF) % (PF + 1)], i0 + u + PF);
+          if (i0 + u < nc) compute(kb[u], vb[u], i0 + u);
+        }
       }
     }
-    const float res = (L > 0.f) ? O / L : 0.f;
-    const int h = h0 + g;
-    if (row_splits == 1) {
-      if constexpr (kF32) out[((size_t)row * a.num_q_heads + h) * D + d] = res;
-      else out[((size_t)row * a.num_q_heads + h) * D + d] = f32_to_bf16(res);
-    } else {
-      const size_t slot = ((size_t)item * a.num_q_heads + h) * num_splits + split;
-      a.ws_o[slot * D + d] = res;
-      if (d == 0) a.ws_lse[slot] = (L > 0.f) ? mx + __builtin_amdgcn_logf(L) : -INFINITY;
+
+    // Each token's weight was counted on all CPR lanes of the token; summing over the
+    // lanes of one chunk (one per token group) gives the piece's totals for that chunk.
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
+    }
+    if (lane < CPR) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float inv = lsum[hh] > 0.f ? 1.f / lsum[hh] : 0.f;
+        if (whole) {
+          T *dst = static_cast<T *>(a.out) + ((size_t)row * a.num_q_heads + h0 + hh) * D +
+                   chunk * EPC;
+          if constexpr (kF32) {
+            *reinterpret_cast<float4 *>(dst) =
+                float4{acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv};
+          } else {
+            uint4 pk;
+            pk.x = pack_bf16x2(acc[hh][0] * inv, acc[hh][1] * inv);
+            pk.y = pack_bf16x2(acc[hh][2] * inv, acc[hh][3] * inv);
+            pk.z = pack_bf16x2(acc[hh][4] * inv, acc[hh][5] * inv);
+            pk.w = pack_bf16x2(acc[hh][6] * inv, acc[hh][7] * inv);
+            *reinterpret_cast<uint4 *>(dst) = pk;
+          }
+        } else {
+          const size_t slot = (size_t)(seg + w) * HG + hh;
+          float *dst = p.ws_o + slot * D + chunk * EPC;
+#pragma unroll
+          for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<float4 *>(dst + e) =
+                float4{acc[hh][e] * inv, acc[hh][e + 1] * inv, acc[hh][e + 2] * inv,
+                       acc[hh][e + 3] * inv};
+          if (lane == 0)
+            p.ws_lse[slot] =
+                lsum[hh] > 0.f ? mref[hh] + __builtin_amdgcn_logf(lsum[hh]) : -INFINITY;
+        }
+      }
     }
   }
 }
 
-// Log-sum-exp merge of the split partials: with per-split (o_i, lse_i) in log2 units,
-// out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i.  One wave per
-// (row, q head); rows with a single split were finished by the decode kernel.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, int items, int bps,
-                                                         int num_splits) {
+// Log-sum-exp merge of the pieces of each segment cut across waves: with per-piece
+// (o_i, lse_i) in log2 units, out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M),
+// M = max_i lse_i.  One wave per (segment, q head of its group); the decode kernel
+// left each segment's first slot and piece count in `seginfo`.
+template <typename T, int D, int HG>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs p) {
   constexpr bool kF32 = std::is_same<T, float>::value;
   constexpr int DW = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int w = blockIdx.x * kWaves + wave;
-  if (w >= items * a.num_q_heads) return;
-  const int item = w / a.num_q_heads;
-  const int h = w - item * a.num_q_heads;
-  int seq, row, row_keys;
-  if (!decode_row<kF32>(a, item, seq, row, row_keys)) return;
-  if (row_keys <= 0) return;
-  const int nblk = min((row_keys + kBlock - 1) / kBlock, num_splits * bps);
-  const int row_splits = (nblk + bps - 1) / bps;
-  if (row_splits <= 1) return;
+  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (gw >= p.items * p.groups * HG) return;
+  const int hh = gw % HG;
+  const int seg = gw / HG;
+  const int first = p.seginfo[2 * seg];
+  const int npieces = p.seginfo[2 * seg + 1];
+  if (npieces == 0) return;
+  const int g = seg / p.items;
+  const int item = seg - g * p.items;
+  int seq, row, keys;
+  bool zero;
+  item_row<kF32>(a, p.item_base + item, seq, row, keys, zero);
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int kvh = g / p.num_head_groups;
+  const int h = kvh * group + (g - kvh * p.num_head_groups) * HG + hh;
+  const size_t base = (size_t)first * HG + hh;  // slot of piece i: base + i * HG
 
-  const size_t base = ((size_t)item * a.num_q_heads + h) * num_splits;
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < row_splits; s0 += 64)
-    if (s0 + lane < row_splits) mx = fmaxf(mx, a.ws_lse[base + s0 + lane]);
+  // pass 1: the largest lse over all pieces
+  float mx = lane < npieces ? p.ws_lse[base + (size_t)lane * HG] : -INFINITY;
+  for (int s0 = 64; s0 < npieces; s0 += 64)
+    if (s0 + lane < npieces) mx = fmaxf(mx, p.ws_lse[base + (size_t)(s0 + lane) * HG]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor(mx, m));
-
+  // pass 2: weighted sum of the pieces' outputs, 8 pieces' loads in flight at a time
+  // (indices past the end are clamped to the last piece and weighted 0)
+  constexpr int kBatch = 8;
   float L = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
-  for (int s0 = 0; s0 < row_splits; s0 += 64) {
-    const float lse = (s0 + lane < row_splits) ? a.ws_lse[base + s0 + lane] : -INFINITY;
-    const float wt = (lse == -INFINITY) ? 0.f : fast_exp2(lse - mx);
-    const int n = min(64, row_splits - s0);
-    for (int j = 0; j < n; ++j) {
-      const float wj = __int_as_float(readlane(__float_as_int(wt), j));
-      L += wj;
-      const float *src = a.ws_o + (base + s0 + j) * D;
+  for (int s0 = 0; s0 < npieces; s0 += kBatch) {
+    float v[kBatch][DW];
+    float lv[kBatch];
 #pragma unroll
-      for (int e = 0; e < DW; ++e) o[e] = fmaf(wj, src[lane + 64 * e], o[e]);
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int j = min(s0 + jj, npieces - 1);
+      const size_t slot = base + (size_t)j * HG;
+      lv[jj] = p.ws_lse[slot];
+      const float *src = p.ws_o + slot * D;
+#pragma unroll
+      for (int e = 0; e < DW; ++e) v[jj][e] = src[lane + 64 * e];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const float wj = (s0 + jj < npieces && lv[jj] != -INFINITY) ? fast_exp2(lv[jj] - mx) : 0.f;
+      L += wj;
+#pragma unroll
+      for (int e = 0; e < DW; ++e) o[e] = fmaf(wj, v[jj][e], o[e]);
     }
   }
   T *out = static_cast<T *>(a.out) + ((size_t)row * a.num_q_heads + h) * D;
@@ -366,33 +498,59 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, int items, 
   }
 }
 
-template <typename T, int D, int HG>
-static hipError_t launch_decode_t(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
-  const int total = p.items * a.num_kv_heads * p.num_head_groups * p.num_splits;
-  if (total == 0) return hipSuccess;
-  const int grid = ((total + 7) / 8) * 8;
-  decode_splitk_kernel<T, D, HG><<<dim3(grid), dim3(kThreads), 0, st>>>(
-      a, p.items, p.num_head_groups, p.blocks_per_split, p.num_splits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_splits <= 1) return e;
-  const int waves = p.items * a.num_q_heads;
-  merge_kernel<T, D><<<dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, st>>>(
-      a, p.items, p.blocks_per_split, p.num_splits);
-  return hipGetLastError();
+template <typename T, int D, int HG, int PF>
+static hipError_t launch_decode_t(const AttnArgs &a, const DecodePlan &pl, hipStream_t st) {
+  for (int base = 0; base < pl.items; base += kMaxStreamItems) {
+    StreamArgs p{};
+    p.item_base = base;
+    p.items = min(kMaxStreamItems, pl.items - base);
+    p.num_head_groups = pl.num_head_groups;
+    p.groups = a.num_kv_heads * pl.num_head_groups;
+    p.ws_o = reinterpret_cast<float *>(static_cast<char *>(pl.workspace) + pl.ws_o_offset);
+    p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(pl.workspace) + pl.ws_lse_offset);
+    p.seginfo =
+        reinterpret_cast<int *>(static_cast<char *>(pl.workspace) + pl.ws_seginfo_offset);
+
+    decode_streamk_kernel<T, D, HG, PF><<<dim3(pl.grid), dim3(kThreads), 0, st>>>(a, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int waves = p.items * p.groups * HG;
+    merge_kernel<T, D, HG><<<dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, st>>>(
+        a, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-template <typename T, int D>
-static hipError_t launch_decode_d(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
-  switch (p.head_group) {
-    case 1: return launch_decode_t<T, D, 1>(a, p, st);
-    case 2: return launch_decode_t<T, D, 2>(a, p, st);
-    case 4: return launch_decode_t<T, D, 4>(a, p, st);
+template <typename T, int D, int HG>
+static hipError_t launch_decode_p(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
+  switch (p.prefetch) {
+    case 1: return launch_decode_t<T, D, HG, 1>(a, p, st);
+    case 2: return launch_decode_t<T, D, HG, 2>(a, p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <typename T, int D>
+static hipError_t launch_decode_d(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
+  // Only the head groups the planner can pick for this element type and head_dim.
+  constexpr int kMaxHG = (512 / (D * (int)sizeof(T))) < 4 ? (512 / (D * (int)sizeof(T))) : 4;
+  switch (p.head_group) {
+    case 1: return launch_decode_p<T, D, 1>(a, p, st);
+    case 2:
+      if constexpr (kMaxHG >= 2) return launch_decode_p<T, D, 2>(a, p, st);
+      break;
+    case 4:
+      if constexpr (kMaxHG >= 4) return launch_decode_p<T, D, 4>(a, p, st);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode(const AttnArgs &a, const DecodePlan &p, pkv_dtype dtype,
                          hipStream_t stream) {
+  if (p.items == 0) return hipSuccess;
   if (dtype == PKV_F32) {
     if (a.head_dim == 64) return launch_decode_d<float, 64>(a, p, stream);
     if (a.head_dim == 128) return launch_decode_d<float, 128>(a, p, stream);

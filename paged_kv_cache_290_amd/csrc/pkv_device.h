@@ -40,6 +40,8 @@ constexpr int kQuadSwap1 = 0xB1;  // lanes (1,0,3,2)
 constexpr int kQuadSwap2 = 0x4E;  // lanes (2,3,0,1)
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i inside each row of 16
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i inside each half row of 8
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
   return __shfl_xor(x, mask, 64);
@@ -63,6 +65,21 @@ __device__ __forceinline__ int readlane(int x, int lane) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer access.  A descriptor covers `bytes` from `base` (stride 0); a load at an
+// offset outside that range fetches nothing from memory and returns zeros.
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family data format word (32-bit elements)
+
+__device__ __forceinline__ buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buffer_load16(buffer_rsrc_t r, int offset) {
+  const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+  return uint4{x.x, x.y, x.z, x.w};
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  This
 // maps the hardware order to a virtual index so that each XCD receives one contiguous

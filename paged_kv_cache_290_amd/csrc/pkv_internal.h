@@ -14,23 +14,26 @@ constexpr int kBlock = PKV_BLOCK_SIZE;  // tokens per physical block
 constexpr int kWaves = 4;               // waves per workgroup in every kernel
 constexpr int kThreads = 64 * kWaves;
 
-// ---------------------------------------------------------------------------
-// Decode (one query row per work item) split-K plan.
+// Decode (single-query rows) plan.
 //
-// A work item is (row, kv head, head group, split).  Rows are sequences with one
-// query (bf16) or every query row (fp32, where prefill rows also take this path).
-// A split covers `blocks_per_split` consecutive logical blocks; the four waves of a
-// workgroup take its blocks round-robin and merge in LDS.  Rows with more than one
-// split leave partial results in the workspace for the merge kernel.
+// Work items ("rows") are sequences with one query (bf16) or every query row (fp32,
+// where prefill rows also take this path).  The decode kernel is persistent: `grid`
+// workgroups of 4 waves split the concatenated blocks of all (kv-head group, row)
+// segments into equal contiguous ranges, one per wave (stream-K).  Pieces of segments
+// cut across waves go to workspace slots that the merge kernel combines.  Rows are
+// handled kMaxStreamItems at a time (one decode + merge launch per chunk).
 // ---------------------------------------------------------------------------
+constexpr int kMaxStreamItems = 2048;
+
 struct DecodePlan {
   int items;            // work rows: num_seqs (bf16) or total_q (fp32)
   int group;            // G = num_q_heads / num_kv_heads
-  int head_group;       // q heads handled together by one workgroup (divides G)
+  int head_group;       // q heads handled together by one wave (divides G)
   int num_head_groups;  // G / head_group
-  int blocks_per_split;
-  int num_splits;       // upper bound over rows, from max_context_len
-  size_t ws_o_offset, ws_lse_offset, ws_bytes;
+  int prefetch;         // blocks in flight per wave while one is computed (1-2)
+  int grid;             // persistent decode workgroups
+  size_t ws_o_offset, ws_lse_offset, ws_seginfo_offset, ws_bytes;
+  void *workspace;      // set by the caller before launching
 };
 
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
@@ -44,12 +47,20 @@ struct AttnArgs {
   const int32_t *block_tables;
   const int32_t *context_lens;
   const int32_t *query_start_loc;
-  float *ws_o;    // [items][Hq][num_splits][D] normalised partial outputs
-  float *ws_lse;  // [items][Hq][num_splits] log2-sum-exp of each partial
   int num_seqs, total_q, num_blocks, max_blocks_per_seq;
   int num_q_heads, num_kv_heads, head_dim;
   int max_query_len;
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
+};
+
+// Per-launch arguments of the decode and merge kernels.
+struct StreamArgs {
+  int item_base, items;  // rows [item_base, item_base + items) of this launch
+  int num_head_groups;   // G / head_group
+  int groups;            // num_kv_heads * num_head_groups
+  float *ws_o;           // [slot][head_group][D] normalised partial outputs
+  float *ws_lse;         // [slot][head_group] log2-sum-exp of each partial
+  int *seginfo;          // [segments][2]: first partial slot, piece count (0: none)
 };
 
 // Launchers (return hipSuccess or the launch error).

@@ -88,8 +88,8 @@ def _attn(**over):
     (dict(q=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(bt=None), _lib.PKV_ERR_INVALID_ARG),
     (dict(mb=0), _lib.PKV_ERR_INVALID_ARG),
-    (dict(maxc=4096), _lib.PKV_ERR_WORKSPACE),          # long context needs split scratch
-    (dict(maxc=4096, ws=8, wsb=16), _lib.PKV_ERR_WORKSPACE),
+    (dict(maxc=4096), _lib.PKV_ERR_WORKSPACE),          # no workspace given
+    (dict(maxc=4096, ws=8, wsb=16), _lib.PKV_ERR_WORKSPACE),  # workspace too small
     (dict(num_seqs=0), _lib.PKV_OK),                   # empty batch: nothing to do
     (dict(total_q=0), _lib.PKV_OK),
 ])
@@ -100,11 +100,12 @@ def test_attention_argument_checks(over, want):
 def test_workspace_size_plan():
     lib = _lib.load()
     ws = lib.paged_attention_workspace_size
-    assert ws(4, 4, 4, 2, 64, 64, _lib.PKV_F32) == 0          # one split per row
-    small = ws(32, 32, 32, 8, 64, 2048, _lib.PKV_BF16)
-    assert small > 0
-    # grows with rows and heads; fp32 rows are per query row
-    assert ws(64, 64, 32, 8, 64, 2048, _lib.PKV_BF16) > small
+    small = ws(4, 4, 4, 2, 64, 64, _lib.PKV_F32)
+    assert small > 0                                           # row prefix + partial slots
+    big = ws(32, 32, 32, 8, 64, 2048, _lib.PKV_BF16)
+    assert big > 0
+    # grows with rows and heads; fp32 items are query rows, bf16 items are sequences
+    assert ws(64, 64, 32, 8, 64, 2048, _lib.PKV_BF16) > big
     assert ws(32, 2048, 32, 8, 64, 2048, _lib.PKV_F32) > ws(32, 2048, 32, 8, 64, 2048,
                                                              _lib.PKV_BF16)
     assert ws(0, 0, 32, 8, 64, 2048, _lib.PKV_BF16) == 0

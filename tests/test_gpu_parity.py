@@ -77,6 +77,14 @@ SMALL = {
                                      num_kv_heads=1, head_dim=64, num_blocks=120,
                                      context_lens=[100, 1300, 33], query_lens=[9, 1, 33],
                                      stale="nan"),
+    # one long sequence: its segments are cut into far more than 64 pieces
+    "long_f32": lambda s: _case("long_f32", s, dtype="f32", num_q_heads=2, num_kv_heads=1,
+                                head_dim=64, num_blocks=2100, context_lens=[33001],
+                                query_lens=[1], stale="nan"),
+    "long_bf16_with_short": lambda s: _case("long_bf16_with_short", s, dtype="bf16",
+                                            num_q_heads=16, num_kv_heads=8, head_dim=128,
+                                            num_blocks=1400, context_lens=[21000, 3, 40],
+                                            query_lens=[1, 1, 1], stale="nan"),
 }
 
 
