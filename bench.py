@@ -252,6 +252,8 @@ def main() -> int:
     ap.add_argument("--only-main", action="store_true",
                     help="skip the other four workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain 256 MiB device copies (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -266,6 +268,14 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": src.numel()}))
+        return 0
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -284,7 +294,7 @@ def main() -> int:
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_for(MAIN),
-            "kernel": "paged_attention_varlen (decode_splitk_kernel + merge_kernel)",
+            "kernel": "paged_attention_varlen (decode_streamk_kernel + merge_kernel)",
             "algorithmic_bytes": abytes, "avg_ms": round(attn_ms, 5)}
     del r
     torch.cuda.empty_cache()

@@ -26,13 +26,16 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
   const int rem = (int)(i - t * per_token);
   const int h = rem / ROW_VECS;
   const int piece = rem - h * ROW_VECS;
+  // The row data does not depend on the slot: load both at once.
+  const uint4 kx = k_new[i];
+  const uint4 vx = v_new[i];
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;  // skipped token (or out of range)
   const int64_t blk = slot / kBlock;
   const int off = (int)(slot % kBlock);
   const int64_t dst = ((blk * num_kv_heads + h) * kBlock + off) * ROW_VECS + piece;
-  k_pool[dst] = k_new[i];
-  v_pool[dst] = v_new[i];
+  k_pool[dst] = kx;
+  v_pool[dst] = vx;
 }
 
 hipError_t launch_kv_write(const void *k_new, const void *v_new, void *k_pool,
