@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kBN = 64;         // keys per tile
 constexpr int kCols = 128;      // columns per workgroup
+constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -57,8 +58,11 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
   constexpr int NCH = D / 8;        // 16-byte chunks per K row
 
-  __shared__ uint4 k_lds[kBN * NCH];     // [key][chunk ^ (key % NCH)]
-  __shared__ uint2 vt_lds[D * (kBN / 4)];  // [dim][keygroup ^ (dim % 16)], 4 keys each
+  constexpr int KCH = kBN * NCH / kThreads;          // K chunks per thread per tile
+  constexpr int VTASK = 16 * NCH;                     // (4-key group, 8-dim chunk) tasks
+  __shared__ uint4 k_lds[2][kBN * NCH];     // [buf][key][chunk ^ (key % NCH)]
+  __shared__ uint2 vt_lds[2][D * (kBN / 4)];  // [buf][dim][keygroup ^ (dim % 16)]
+  __shared__ int s_tbl[kTblCache];          // block-table entries of this workgroup
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -146,49 +150,104 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
   float mref[2] = {-INFINITY, -INFINITY};
   float lsum[2] = {0.f, 0.f};
 
-  auto row_ptr = [&](const uint16_t *pool, int kidx) {
-    int pb = tbl[kidx / kBlock];
-    pb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
-    return reinterpret_cast<const uint4 *>(
-        pool + (((size_t)pb * a.num_kv_heads + kvh) * kBlock + (kidx % kBlock)) * D);
+  // Block-table entries of the keys this workgroup reads, cached in LDS kTblCache at a
+  // time (refilled every kTblCache/4 tiles); invalid entries read block 0.
+  const int nblk = (kv_end + kBlock - 1) / kBlock;
+  auto fill_tbl = [&](int first_blk) {
+    for (int i = threadIdx.x; i < kTblCache; i += kThreads) {
+      const int lb = first_blk + i;
+      int pb = lb < nblk ? tbl[lb] : 0;
+      s_tbl[i] = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
+    }
   };
+  // Staging of a 64-key tile, in two halves so the loads of tile kt+1 are in flight
+  // while tile kt is computed.  fetch: global -> registers.  Every load is issued
+  // unconditionally (a key past kv_end re-reads the last valid row and is zeroed
+  // afterwards), so all of a tile's loads leave back to back.  stage: registers -> LDS
+  // buffer `buf`: K row-major with the chunk index XOR-swizzled by key, V transposed
+  // (4 keys of one dim per 8 bytes) with key groups swizzled by dim.
+  uint4 kreg[KCH];
+  uint4 vreg[4];
+#define PKV_KEY_ROW(pool, kidx)                                                          \
+  (reinterpret_cast<const uint4 *>(                                                      \
+      (pool) + (((size_t)s_tbl[((kidx) / kBlock) % kTblCache] * a.num_kv_heads + kvh) *  \
+                    kBlock + ((kidx) % kBlock)) * D))
+#define PKV_FETCH(kt)                                                                    \
+  do {                                                                                   \
+    const int k0_ = (kt) * kBN;                                                          \
+    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
+      const int c = threadIdx.x + kThreads * i;                                          \
+      const int key = c / NCH;                                                           \
+      const int kidx = min(k0_ + key, kv_end - 1);                                       \
+      kreg[i] = PKV_KEY_ROW(kpool, kidx)[c - key * NCH];                                 \
+    }                                                                                    \
+    if (threadIdx.x < VTASK) {                                                           \
+      const int kg = threadIdx.x & 15;                                                   \
+      const int j = threadIdx.x >> 4;                                                    \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
+        const int kidx = min(k0_ + 4 * kg + i, kv_end - 1);                              \
+        vreg[i] = PKV_KEY_ROW(vpool, kidx)[j];                                           \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
+#define PKV_STAGE(kt, buf)                                                               \
+  do {                                                                                   \
+    const int k0_ = (kt) * kBN;                                                          \
+    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
+      const int c = threadIdx.x + kThreads * i;                                          \
+      const int key = c / NCH;                                                           \
+      const int ch = c - key * NCH;                                                      \
+      const bool live = k0_ + key < kv_end;                                              \
+      const uint4 x = kreg[i];                                                           \
+      k_lds[buf][key * NCH + (ch ^ (key % NCH))] =                                       \
+          uint4{live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u};     \
+    }                                                                                    \
+    if (threadIdx.x < VTASK) {                                                           \
+      const int kg = threadIdx.x & 15;                                                   \
+      const int j = threadIdx.x >> 4;                                                    \
+      uint32_t w[4][4];                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
+        const bool live = k0_ + 4 * kg + i < kv_end;                                     \
+        w[i][0] = live ? vreg[i].x : 0u;                                                 \
+        w[i][1] = live ? vreg[i].y : 0u;                                                 \
+        w[i][2] = live ? vreg[i].z : 0u;                                                 \
+        w[i][3] = live ? vreg[i].w : 0u;                                                 \
+      }                                                                                  \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
+        const int d0 = 8 * j + 2 * e;                                                    \
+        const int d1 = d0 + 1;                                                           \
+        vt_lds[buf][d0 * 16 + (kg ^ (d0 & 15))] =                                        \
+            uint2{(w[0][e] & 0xffffu) | (w[1][e] << 16),                                 \
+                  (w[2][e] & 0xffffu) | (w[3][e] << 16)};                                \
+        vt_lds[buf][d1 * 16 + (kg ^ (d1 & 15))] =                                        \
+            uint2{(w[0][e] >> 16) | (w[1][e] & 0xffff0000u),                             \
+                  (w[2][e] >> 16) | (w[3][e] & 0xffff0000u)};                            \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
+
+  fill_tbl(0);
+  __syncthreads();
+  if (nkt > 0) {
+    PKV_FETCH(0);
+    PKV_STAGE(0, 0);
+  }
+  __syncthreads();
+  // Retire every outstanding load (the query fragments in particular) on all paths
+  // here.  Otherwise the wait counters merged at the loop head still see the query
+  // loads in flight, and each MFMA that reads them waits for the next tile's
+  // prefetch as well, which undoes the overlap.
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kBN;
-    __syncthreads();  // the previous tile is no longer read
-    // Stage K: 64 keys x NCH chunks, chunk index XOR-swizzled by key.
-    for (int c = threadIdx.x; c < kBN * NCH; c += kThreads) {
-      const int key = c / NCH;
-      const int ch = c - key * NCH;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (k0 + key < kv_end) val = row_ptr(kpool, k0 + key)[ch];
-      k_lds[key * NCH + (ch ^ (key % NCH))] = val;
+    const int buf = kt & 1;
+    // Refill the table cache before the first fetch that needs new entries.
+    if (kt + 1 < nkt && ((kt + 1) * (kBN / kBlock)) % kTblCache == 0) {
+      fill_tbl((kt + 1) * (kBN / kBlock));
+      __syncthreads();
     }
-    // Stage V transposed: task = (group of 4 keys, chunk of 8 dims).
-    for (int t = threadIdx.x; t < 16 * NCH; t += kThreads) {
-      const int kg = t & 15;
-      const int j = t >> 4;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kidx = k0 + 4 * kg + i;
-        uint4 x = {0u, 0u, 0u, 0u};
-        if (kidx < kv_end) x = row_ptr(vpool, kidx)[j];
-        w[i][0] = x.x; w[i][1] = x.y; w[i][2] = x.z; w[i][3] = x.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d0 = 8 * j + 2 * e;
-        const int d1 = d0 + 1;
-        const uint2 even = {(w[0][e] & 0xffffu) | (w[1][e] << 16),
-                            (w[2][e] & 0xffffu) | (w[3][e] << 16)};
-        const uint2 odd = {(w[0][e] >> 16) | (w[1][e] & 0xffff0000u),
-                           (w[2][e] >> 16) | (w[3][e] & 0xffff0000u)};
-        vt_lds[d0 * 16 + (kg ^ (d0 & 15))] = even;
-        vt_lds[d1 * 16 + (kg ^ (d1 & 15))] = odd;
-      }
-    }
-    __syncthreads();
+    if (kt + 1 < nkt) PKV_FETCH(kt + 1);  // in flight while this tile is computed
 
     // S^T tile: sacc[sub][cg] element r <-> key k0 + 16*sub + 4*lg + r, column cg.
     f32x4_t sacc[4][2];
@@ -201,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const int key = sub * 16 + l16;
-        const bf16x8_t af = as_bf16x8(k_lds[key * NCH + ((4 * ks + lg) ^ (key % NCH))]);
+        const bf16x8_t af = as_bf16x8(k_lds[buf][key * NCH + ((4 * ks + lg) ^ (key % NCH))]);
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = mfma16(af, qf[cg][ks], sacc[sub][cg]);
       }
@@ -274,13 +333,15 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
       const int dim = mt * 16 + l16;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint2 a0 = vt_lds[dim * 16 + ((8 * ks2 + lg) ^ (dim & 15))];
-        const uint2 a1 = vt_lds[dim * 16 + ((8 * ks2 + 4 + lg) ^ (dim & 15))];
+        const uint2 a0 = vt_lds[buf][dim * 16 + ((8 * ks2 + lg) ^ (dim & 15))];
+        const uint2 a1 = vt_lds[buf][dim * 16 + ((8 * ks2 + 4 + lg) ^ (dim & 15))];
         const bf16x8_t af = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg) o[mt][cg] = mfma16(af, pf[cg][ks2], o[mt][cg]);
       }
     }
+    if (kt + 1 < nkt) PKV_STAGE(kt + 1, buf ^ 1);
+    __syncthreads();  // tile kt+1 staged; everyone is done reading tile kt
   }
 
   // Epilogue: column totals, normalise, bf16 store of 4 consecutive dims per tile.
@@ -301,6 +362,10 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
     }
   }
 }
+
+#undef PKV_KEY_ROW
+#undef PKV_FETCH
+#undef PKV_STAGE
 
 template <int D, int HGP>
 static hipError_t launch_prefill_t(const AttnArgs &a, hipStream_t st) {
