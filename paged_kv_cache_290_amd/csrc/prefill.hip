@@ -10,14 +10,21 @@
 //  * Serving-engine KV page (ttlab), section 2, "blocks and block table": keys and
 //    values are read from 16-token blocks through the block table.
 //
-// One workgroup (4 waves) owns 128 columns = (query row, q head) pairs of one KV
-// head: HGP heads x (128/HGP) consecutive rows.  Each wave owns 32 columns.  The
-// workgroup walks 64-key tiles (4 physical blocks): K is staged in LDS row-major and
-// V transposed (both XOR-swizzled so the MFMA fragment reads are bank-conflict free),
-// then each wave computes the transposed score tile S^T = K Q^T and the update
-// O^T += V^T P^T with v_mfma_f32_16x16x32_bf16.  Working on transposes lets the
-// score accumulator be reused directly as the B operand of the second product: both
-// hold one column per lane%16 and the same key slots.
+// One workgroup (8 waves, two per SIMD) owns 128 columns = (query row, q head) pairs
+// of one KV head: HGP heads x (128/HGP) consecutive rows.  The keys are walked in
+// 128-key steps (8 physical blocks).  Waves 0-3 take the first 64 keys of a step and
+// waves 4-7 the second 64, each wave over 32 columns, so every SIMD holds one wave of
+// each half and can run one wave's softmax while the other's matrix products issue.
+// The two halves keep separate online-softmax states (an in-workgroup split of the
+// key range) that are merged through LDS at the end.
+//
+// K is staged in LDS row-major and V transposed (both XOR-swizzled so the MFMA
+// fragment reads are bank-conflict free); the next step's global loads are in flight
+// while the current step is computed (double-buffered LDS).  Each wave computes the
+// transposed score tile S^T = K Q^T and the update O^T += V^T P^T with
+// v_mfma_f32_16x16x32_bf16.  Working on transposes lets the score accumulator feed
+// the second product directly: both hold one column per lane%16 and the same key
+// slots.
 //
 // MFMA 16x16x32 operand layout (lane l, g = l/16): A row l%16 and B column l%16 each
 // hold 8 k-slots (g, e); the contraction pairs equal slots, so any fixed assignment
@@ -25,8 +32,11 @@
 // rows 4g..4g+3 of column l%16.
 //
 // Softmax is the online form in log2 units with a lazily raised per-column reference
-// max (raised only when a score exceeds it by more than kSlack), P is rounded to
-// bf16 for the second product, accumulation is fp32, output is bf16 (RNE).
+// max (raised only when a score exceeds it by more than kSlack, so the cross-lane
+// maximum is only formed then).  P is rounded to bf16 for the second product and the
+// softmax denominator sums those same rounded weights (dot2 with ones), accumulation
+// is fp32, output is bf16 (RNE).  A negative scale is folded into the
+// sign of q (exact in bf16) so the kernel works with |scale|.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -34,10 +44,13 @@ namespace pkv {
 
 namespace {
 
-constexpr int kBN = 64;         // keys per tile
+constexpr int kPThreads = 512;  // 8 waves
+constexpr int kHalfKeys = 64;   // keys per wave group per step
+constexpr int kStepKeys = 128;  // keys per step
 constexpr int kCols = 128;      // columns per workgroup
 constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
+constexpr uint32_t kBf16Ones = 0x3F803F80u;  // two bf16 1.0
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -47,25 +60,145 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) {
   return __builtin_bit_cast(bf16x8_t, x);
 }
 
+// One wave's update with a 64-key tile: kb = K tile [key][chunk ^ key%NCH], vb = V^T
+// tile [dim][keygroup ^ dim%16]; kbase = position of the tile's first key.  MASK
+// applies the causal and length masks (tiles that reach past the first column's
+// position or past kv_end).
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_update(const uint4 *kb, const uint2 *vb,
+                                            const bf16x8_t (&qf)[2][D / 32],
+                                            f32x4_t (&o)[D / 16][2], float (&mref)[2],
+                                            float (&mneg)[2], float (&lsum)[2], float sc,
+                                            int kbase, const int (&col_pos)[2], int kv_end,
+                                            int l16, int lg) {
+  constexpr int KS = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int NCH = D / 8;
+
+  // S^T tile: sacc[sub][cg] element r <-> key kbase + 16*sub + 4*lg + r, column cg.
+  f32x4_t sacc[4][2];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const int key = sub * 16 + l16;
+      const bf16x8_t af = as_bf16x8(kb[key * NCH + ((4 * ks + lg) ^ (key % NCH))]);
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = mfma16(af, qf[cg][ks], sacc[sub][cg]);
+    }
+  }
+
+  // Per-lane maximum of the scaled scores (log2 units).
+  float lmx[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    if (MASK) {
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kbase + sub * 16 + 4 * lg + r;
+          if (key > col_pos[cg] || key >= kv_end) sacc[sub][cg][r] = -INFINITY;
+        }
+    }
+    float m = sacc[0][cg][0];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (sub | r) m = fmaxf(m, sacc[sub][cg][r]);
+    lmx[cg] = m * sc;
+  }
+  const bool need = (lmx[0] > mref[0] + kSlack) || (lmx[1] > mref[1] + kSlack);
+  if (wave_any(need)) {
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      float m = lmx[cg];
+      m = fmaxf(m, shfl_xor(m, 16));
+      m = fmaxf(m, shfl_xor(m, 32));
+      const float mn = fmaxf(mref[cg], m);
+      const float alpha = (mref[cg] == -INFINITY) ? 0.f : fast_exp2(mref[cg] - mn);
+      mref[cg] = mn;
+      mneg[cg] = (mn == -INFINITY) ? 0.f : -mn;
+      lsum[cg] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[mt][cg] *= alpha;
+    }
+  }
+
+  // P = exp2(s * sc - mref), bf16 packed in the k-slot order of the V^T fragments.
+  bf16x8_t pf[2][2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    float p[16];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p[sub * 4 + r] = fast_exp2(fmaf(sacc[sub][cg][r], sc, mneg[cg]));
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint4 packed;
+      packed.x = pack_bf16x2(p[8 * ks2 + 0], p[8 * ks2 + 1]);
+      packed.y = pack_bf16x2(p[8 * ks2 + 2], p[8 * ks2 + 3]);
+      packed.z = pack_bf16x2(p[8 * ks2 + 4], p[8 * ks2 + 5]);
+      packed.w = pack_bf16x2(p[8 * ks2 + 6], p[8 * ks2 + 7]);
+      pf[cg][ks2] = as_bf16x8(packed);
+      // The denominator sums the same bf16-rounded weights the numerator uses.
+      lsum[cg] = dot2_bf16(packed.x, kBf16Ones, lsum[cg]);
+      lsum[cg] = dot2_bf16(packed.y, kBf16Ones, lsum[cg]);
+      lsum[cg] = dot2_bf16(packed.z, kBf16Ones, lsum[cg]);
+      lsum[cg] = dot2_bf16(packed.w, kBf16Ones, lsum[cg]);
+    }
+  }
+
+  // O^T += V^T P^T: A row = dim, k-slots (lg, e) <-> keys 32*ks2 + 4*lg + e (e < 4)
+  // and 32*ks2 + 16 + 4*lg + (e - 4), matching the slots of pf.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int dim = mt * 16 + l16;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const uint2 a0 = vb[dim * 16 + ((8 * ks2 + lg) ^ (dim & 15))];
+      const uint2 a1 = vb[dim * 16 + ((8 * ks2 + 4 + lg) ^ (dim & 15))];
+      const bf16x8_t af = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) o[mt][cg] = mfma16(af, pf[cg][ks2], o[mt][cg]);
+    }
+  }
+}
+
 }  // namespace
 
 template <int D, int HGP>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
-                                                                int num_head_groups,
-                                                                int tile_slots) {
+__global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
+                                                                 int num_head_groups,
+                                                                 int tile_slots) {
   constexpr int BMQ = kCols / HGP;  // query rows per workgroup
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
   constexpr int NCH = D / 8;        // 16-byte chunks per K row
-
-  constexpr int KCH = kBN * NCH / kThreads;          // K chunks per thread per tile
-  constexpr int VTASK = 16 * NCH;                     // (4-key group, 8-dim chunk) tasks
-  __shared__ uint4 k_lds[2][kBN * NCH];     // [buf][key][chunk ^ (key % NCH)]
-  __shared__ uint2 vt_lds[2][D * (kBN / 4)];  // [buf][dim][keygroup ^ (dim % 16)]
-  __shared__ int s_tbl[kTblCache];          // block-table entries of this workgroup
+  constexpr int K_U4 = kHalfKeys * NCH;               // uint4 per K tile
+  constexpr int V_U2 = D * (kHalfKeys / 4);           // uint2 per V^T tile
+  constexpr int KCH = kStepKeys * NCH / kPThreads;    // K chunks per thread per step
+  constexpr int VTH = 16 * NCH;                       // (4-key group, chunk) tasks per half
+  constexpr int LDS_U4 = 4 * K_U4 + 2 * V_U2;         // [buf][half] K tiles, then V^T
+  constexpr int XF = MT * 8 + 4;                      // floats per lane in the merge
+  static_assert(4 * XF * 64 * 4 <= LDS_U4 * 16, "merge exchange must fit the tiles");
+  static_assert(2 * VTH <= kPThreads, "one V task per thread at most");
+  __shared__ uint4 lds[LDS_U4];
+  __shared__ int s_tbl[kTblCache];  // block-table entries of this workgroup
+  uint4 *const k_lds = lds;                                       // [buf*2+half][K_U4]
+  uint2 *const vt_lds = reinterpret_cast<uint2 *>(lds + 4 * K_U4);  // [buf*2+half][V_U2]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int half = wave >> 2;  // which 64 keys of each step
+  const int cw = wave & 3;     // which 32 columns
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
@@ -104,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
   bool col_ok[2];
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg) {
-    const int c = wave * 32 + cg * 16 + l16;
+    const int c = cw * 32 + cg * 16 + l16;
     const int g = c / BMQ;
     int qi = c - g * BMQ;
     col_ok[cg] = qi < nq;
@@ -115,15 +248,20 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
   }
 
   if (ctx < q_len) {  // precondition broken: defined as zeros
+    if (half == 0) {
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
-      if (col_ok[cg])
-        for (int d = lg; d < D; d += 4)
-          out[((size_t)col_row[cg] * a.num_q_heads + col_head[cg]) * D + d] = 0;
+      for (int cg = 0; cg < 2; ++cg)
+        if (col_ok[cg])
+          for (int d = lg; d < D; d += 4)
+            out[((size_t)col_row[cg] * a.num_q_heads + col_head[cg]) * D + d] = 0;
+    }
     return;
   }
 
-  // Q^T fragments (B operand of S^T): column's row, dims 32*ks + 8*lg + 0..7.
+  // Q^T fragments (B operand of S^T): column's row, dims 32*ks + 8*lg + 0..7, with
+  // the sign of a negative scale folded in.
+  const float sc = fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   bf16x8_t qf[2][KS];
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg) {
@@ -131,13 +269,17 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
         static_cast<const uint16_t *>(a.q) +
         ((size_t)col_row[cg] * a.num_q_heads + col_head[cg]) * D);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[cg][ks] = as_bf16x8(src[4 * ks + lg]);
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 x = src[4 * ks + lg];
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+      qf[cg][ks] = as_bf16x8(x);
+    }
   }
 
   const int pos_first = ctx - q_len + qi0;
   const int ctx_eff = min(ctx, a.max_blocks_per_seq * kBlock);
   const int kv_end = min(pos_first + nq, ctx_eff);
-  const int nkt = (kv_end + kBN - 1) / kBN;
+  const int nst = (kv_end + kStepKeys - 1) / kStepKeys;
   const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
   const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
@@ -148,221 +290,177 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(AttnArgs a,
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) o[mt][cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mref[2] = {-INFINITY, -INFINITY};
+  float mneg[2] = {0.f, 0.f};
   float lsum[2] = {0.f, 0.f};
 
   // Block-table entries of the keys this workgroup reads, cached in LDS kTblCache at a
-  // time (refilled every kTblCache/4 tiles); invalid entries read block 0.
+  // time (refilled every kTblCache/8 steps); invalid entries read block 0.
   const int nblk = (kv_end + kBlock - 1) / kBlock;
-  auto fill_tbl = [&](int first_blk) {
-    for (int i = threadIdx.x; i < kTblCache; i += kThreads) {
-      const int lb = first_blk + i;
-      int pb = lb < nblk ? tbl[lb] : 0;
-      s_tbl[i] = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
-    }
-  };
-  // Staging of a 64-key tile, in two halves so the loads of tile kt+1 are in flight
-  // while tile kt is computed.  fetch: global -> registers.  Every load is issued
-  // unconditionally (a key past kv_end re-reads the last valid row and is zeroed
-  // afterwards), so all of a tile's loads leave back to back.  stage: registers -> LDS
-  // buffer `buf`: K row-major with the chunk index XOR-swizzled by key, V transposed
-  // (4 keys of one dim per 8 bytes) with key groups swizzled by dim.
+  const int tid = threadIdx.x;
+#define PKV_FILL_TBL(first_blk)                                                          \
+  do {                                                                                   \
+    if (tid < kTblCache) {                                                               \
+      const int lb_ = (first_blk) + tid;                                                 \
+      const int pb_ = lb_ < nblk ? tbl[lb_] : 0;                                         \
+      s_tbl[tid] = (pb_ < 0 || pb_ >= a.num_blocks) ? 0 : pb_;                           \
+    }                                                                                    \
+  } while (0)
+
+  // Staging of a 128-key step.  fetch: global -> registers, every load unconditional
+  // (a key past kv_end re-reads the last valid row and is zeroed when staged), so all
+  // of a step's loads leave back to back.  stage: registers -> LDS buffer `buf`: K
+  // row-major with the chunk index XOR-swizzled by key, V transposed (4 keys of one
+  // dim per 8 bytes) with key groups swizzled by dim; keys 0-63 of the step go to half
+  // 0, keys 64-127 to half 1.
   uint4 kreg[KCH];
   uint4 vreg[4];
+  const bool vtask = tid < 2 * VTH;
+  const int vhalf = tid / VTH;
+  const int vkg = tid & 15;
+  const int vj = (tid % VTH) >> 4;
 #define PKV_KEY_ROW(pool, kidx)                                                          \
   (reinterpret_cast<const uint4 *>(                                                      \
       (pool) + (((size_t)s_tbl[((kidx) / kBlock) % kTblCache] * a.num_kv_heads + kvh) *  \
                     kBlock + ((kidx) % kBlock)) * D))
-#define PKV_FETCH(kt)                                                                    \
+#define PKV_FETCH(st)                                                                    \
   do {                                                                                   \
-    const int k0_ = (kt) * kBN;                                                          \
+    const int k0_ = (st) * kStepKeys;                                                    \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const int c = threadIdx.x + kThreads * i;                                          \
+      const int c = tid + kPThreads * i;                                                 \
       const int key = c / NCH;                                                           \
       const int kidx = min(k0_ + key, kv_end - 1);                                       \
       kreg[i] = PKV_KEY_ROW(kpool, kidx)[c - key * NCH];                                 \
     }                                                                                    \
-    if (threadIdx.x < VTASK) {                                                           \
-      const int kg = threadIdx.x & 15;                                                   \
-      const int j = threadIdx.x >> 4;                                                    \
+    if (vtask) {                                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
-        const int kidx = min(k0_ + 4 * kg + i, kv_end - 1);                              \
-        vreg[i] = PKV_KEY_ROW(vpool, kidx)[j];                                           \
+        const int kidx = min(k0_ + kHalfKeys * vhalf + 4 * vkg + i, kv_end - 1);         \
+        vreg[i] = PKV_KEY_ROW(vpool, kidx)[vj];                                          \
       }                                                                                  \
     }                                                                                    \
   } while (0)
-#define PKV_STAGE(kt, buf)                                                               \
+#define PKV_STAGE(st, buf)                                                               \
   do {                                                                                   \
-    const int k0_ = (kt) * kBN;                                                          \
+    const int k0_ = (st) * kStepKeys;                                                    \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const int c = threadIdx.x + kThreads * i;                                          \
+      const int c = tid + kPThreads * i;                                                 \
       const int key = c / NCH;                                                           \
       const int ch = c - key * NCH;                                                      \
+      const int kh = key / kHalfKeys;                                                    \
+      const int kl = key % kHalfKeys;                                                    \
       const bool live = k0_ + key < kv_end;                                              \
       const uint4 x = kreg[i];                                                           \
-      k_lds[buf][key * NCH + (ch ^ (key % NCH))] =                                       \
+      k_lds[((buf) * 2 + kh) * K_U4 + kl * NCH + (ch ^ (kl % NCH))] =                    \
           uint4{live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u};     \
     }                                                                                    \
-    if (threadIdx.x < VTASK) {                                                           \
-      const int kg = threadIdx.x & 15;                                                   \
-      const int j = threadIdx.x >> 4;                                                    \
+    if (vtask) {                                                                         \
       uint32_t w[4][4];                                                                  \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
-        const bool live = k0_ + 4 * kg + i < kv_end;                                     \
+        const bool live = k0_ + kHalfKeys * vhalf + 4 * vkg + i < kv_end;                \
         w[i][0] = live ? vreg[i].x : 0u;                                                 \
         w[i][1] = live ? vreg[i].y : 0u;                                                 \
         w[i][2] = live ? vreg[i].z : 0u;                                                 \
         w[i][3] = live ? vreg[i].w : 0u;                                                 \
       }                                                                                  \
+      uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2;                                  \
       _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
-        const int d0 = 8 * j + 2 * e;                                                    \
+        const int d0 = 8 * vj + 2 * e;                                                   \
         const int d1 = d0 + 1;                                                           \
-        vt_lds[buf][d0 * 16 + (kg ^ (d0 & 15))] =                                        \
+        vt_[d0 * 16 + (vkg ^ (d0 & 15))] =                                               \
             uint2{(w[0][e] & 0xffffu) | (w[1][e] << 16),                                 \
                   (w[2][e] & 0xffffu) | (w[3][e] << 16)};                                \
-        vt_lds[buf][d1 * 16 + (kg ^ (d1 & 15))] =                                        \
+        vt_[d1 * 16 + (vkg ^ (d1 & 15))] =                                               \
             uint2{(w[0][e] >> 16) | (w[1][e] & 0xffff0000u),                             \
                   (w[2][e] >> 16) | (w[3][e] & 0xffff0000u)};                            \
       }                                                                                  \
     }                                                                                    \
   } while (0)
 
-  fill_tbl(0);
+  PKV_FILL_TBL(0);
   __syncthreads();
-  if (nkt > 0) {
+  if (nst > 0) {
     PKV_FETCH(0);
     PKV_STAGE(0, 0);
   }
   __syncthreads();
   // Retire every outstanding load (the query fragments in particular) on all paths
   // here.  Otherwise the wait counters merged at the loop head still see the query
-  // loads in flight, and each MFMA that reads them waits for the next tile's
+  // loads in flight, and each MFMA that reads them waits for the next step's
   // prefetch as well, which undoes the overlap.
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * kBN;
-    const int buf = kt & 1;
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
     // Refill the table cache before the first fetch that needs new entries.
-    if (kt + 1 < nkt && ((kt + 1) * (kBN / kBlock)) % kTblCache == 0) {
-      fill_tbl((kt + 1) * (kBN / kBlock));
+    if (st + 1 < nst && ((st + 1) * (kStepKeys / kBlock)) % kTblCache == 0) {
+      PKV_FILL_TBL((st + 1) * (kStepKeys / kBlock));
       __syncthreads();
     }
-    if (kt + 1 < nkt) PKV_FETCH(kt + 1);  // in flight while this tile is computed
+    if (st + 1 < nst) PKV_FETCH(st + 1);  // in flight while this step is computed
 
-    // S^T tile: sacc[sub][cg] element r <-> key k0 + 16*sub + 4*lg + r, column cg.
-    f32x4_t sacc[4][2];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const int key = sub * 16 + l16;
-        const bf16x8_t af = as_bf16x8(k_lds[buf][key * NCH + ((4 * ks + lg) ^ (key % NCH))]);
-#pragma unroll
-        for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = mfma16(af, qf[cg][ks], sacc[sub][cg]);
-      }
+    const int kbase = st * kStepKeys + half * kHalfKeys;
+    if (kbase < kv_end) {
+      const uint4 *kb = k_lds + (buf * 2 + half) * K_U4;
+      const uint2 *vb = vt_lds + (buf * 2 + half) * V_U2;
+      const bool edge = (kbase + kHalfKeys - 1 > pos_first) || (kbase + kHalfKeys > kv_end);
+      if (edge)
+        tile_update<D, true>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
+                             l16, lg);
+      else
+        tile_update<D, false>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
+                              l16, lg);
     }
-
-    const bool edge = (k0 + kBN - 1 > pos_first) || (k0 + kBN > kv_end);
-    float p[2][16];
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = sacc[sub][cg][r] * a.scale_log2;
-          if (edge) {
-            const int key = k0 + sub * 16 + 4 * lg + r;
-            if (key > col_pos[cg] || key >= kv_end) x = -INFINITY;
-          }
-          p[cg][sub * 4 + r] = x;
-        }
-    }
-    float mx[2];
-    bool need = false;
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      float m = p[cg][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, p[cg][i]);
-      m = fmaxf(m, shfl_xor(m, 16));
-      m = fmaxf(m, shfl_xor(m, 32));
-      mx[cg] = m;
-      need |= m > mref[cg] + kSlack;
-    }
-    if (wave_any(need)) {
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
-        const float mn = fmaxf(mref[cg], mx[cg]);
-        const float alpha = (mref[cg] == -INFINITY) ? 0.f : fast_exp2(mref[cg] - mn);
-        mref[cg] = mn;
-        lsum[cg] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[mt][cg] *= alpha;
-      }
-    }
-    bf16x8_t pf[2][2];
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[cg][i] = fast_exp2(p[cg][i] - mref[cg]);
-        s += p[cg][i];
-      }
-      lsum[cg] += s;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint4 packed;
-        packed.x = pack_bf16x2(p[cg][8 * ks2 + 0], p[cg][8 * ks2 + 1]);
-        packed.y = pack_bf16x2(p[cg][8 * ks2 + 2], p[cg][8 * ks2 + 3]);
-        packed.z = pack_bf16x2(p[cg][8 * ks2 + 4], p[cg][8 * ks2 + 5]);
-        packed.w = pack_bf16x2(p[cg][8 * ks2 + 6], p[cg][8 * ks2 + 7]);
-        pf[cg][ks2] = as_bf16x8(packed);
-      }
-    }
-
-    // O^T += V^T P^T: A row = dim, k-slots (lg, e) <-> keys 32*ks2 + 4*lg + e (e < 4)
-    // and 32*ks2 + 16 + 4*lg + (e - 4), matching the slots of pf.
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int dim = mt * 16 + l16;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint2 a0 = vt_lds[buf][dim * 16 + ((8 * ks2 + lg) ^ (dim & 15))];
-        const uint2 a1 = vt_lds[buf][dim * 16 + ((8 * ks2 + 4 + lg) ^ (dim & 15))];
-        const bf16x8_t af = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
-#pragma unroll
-        for (int cg = 0; cg < 2; ++cg) o[mt][cg] = mfma16(af, pf[cg][ks2], o[mt][cg]);
-      }
-    }
-    if (kt + 1 < nkt) PKV_STAGE(kt + 1, buf ^ 1);
-    __syncthreads();  // tile kt+1 staged; everyone is done reading tile kt
+    if (st + 1 < nst) PKV_STAGE(st + 1, buf ^ 1);
+    __syncthreads();  // step st+1 staged; everyone is done reading step st
   }
 
-  // Epilogue: column totals, normalise, bf16 store of 4 consecutive dims per tile.
+  // Merge the two halves' states through LDS (the tiles are no longer read: the loop
+  // ended on a barrier), then normalise and store bf16, 4 consecutive dims per tile.
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg) {
-    float L = lsum[cg];
-    L += shfl_xor(L, 16);
-    L += shfl_xor(L, 32);
+    lsum[cg] += shfl_xor(lsum[cg], 16);
+    lsum[cg] += shfl_xor(lsum[cg], 32);
+  }
+  float *xch = reinterpret_cast<float *>(lds) + cw * XF * 64 + lane;
+  if (half == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xch[((mt * 2 + cg) * 4 + r) * 64] = o[mt][cg][r];
+    xch[(MT * 8 + 0) * 64] = mref[0];
+    xch[(MT * 8 + 1) * 64] = mref[1];
+    xch[(MT * 8 + 2) * 64] = lsum[0];
+    xch[(MT * 8 + 3) * 64] = lsum[1];
+  }
+  __syncthreads();
+  if (half == 1) return;
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    const float m1 = xch[(MT * 8 + cg) * 64];
+    const float l1 = xch[(MT * 8 + 2 + cg) * 64];
+    const float mx = fmaxf(mref[cg], m1);
+    const float a0 = (mref[cg] == -INFINITY) ? 0.f : fast_exp2(mref[cg] - mx);
+    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mx);
+    const float L = a0 * lsum[cg] + a1 * l1;
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     if (!col_ok[cg]) continue;
     uint16_t *dst = out + ((size_t)col_row[cg] * a.num_q_heads + col_head[cg]) * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        y[r] = (a0 * o[mt][cg][r] + a1 * xch[((mt * 2 + cg) * 4 + r) * 64]) * inv;
       uint2 packed;
-      packed.x = pack_bf16x2(o[mt][cg][0] * inv, o[mt][cg][1] * inv);
-      packed.y = pack_bf16x2(o[mt][cg][2] * inv, o[mt][cg][3] * inv);
+      packed.x = pack_bf16x2(y[0], y[1]);
+      packed.y = pack_bf16x2(y[2], y[3]);
       *reinterpret_cast<uint2 *>(dst + mt * 16 + 4 * lg) = packed;
     }
   }
 }
 
+#undef PKV_FILL_TBL
 #undef PKV_KEY_ROW
 #undef PKV_FETCH
 #undef PKV_STAGE
@@ -375,7 +473,7 @@ static hipError_t launch_prefill_t(const AttnArgs &a, hipStream_t st) {
   const int total = slots * a.num_kv_heads * nhg;
   if (total == 0) return hipSuccess;
   const int grid = ((total + 7) / 8) * 8;
-  prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kThreads), 0, st>>>(a, nhg, slots);
+  prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kPThreads), 0, st>>>(a, nhg, slots);
   return hipGetLastError();
 }
 
