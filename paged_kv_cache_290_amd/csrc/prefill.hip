@@ -51,6 +51,10 @@ constexpr int kCols = 128;      // columns per workgroup
 constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
 constexpr uint32_t kBf16Ones = 0x3F803F80u;  // two bf16 1.0
+// v_perm_b32 selectors: low halves of (s1, s0) -> (s1.lo, s0.lo), high halves likewise
+// (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
+constexpr uint32_t kPermLo = 0x05040100u;
+constexpr uint32_t kPermHi = 0x07060302u;
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -306,71 +310,83 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     }                                                                                    \
   } while (0)
 
-  // Staging of a 128-key step.  fetch: global -> registers, every load unconditional
-  // (a key past kv_end re-reads the last valid row and is zeroed when staged), so all
+  // Staging of a 128-key step.  fetch: global -> registers, every load unconditional:
+  // a key past kv_end reads a row of its block, or of block 0 when its table entry
+  // is past the sequence (the cache holds 0 there), and is zeroed when staged, so all
   // of a step's loads leave back to back.  stage: registers -> LDS buffer `buf`: K
   // row-major with the chunk index XOR-swizzled by key, V transposed (4 keys of one
   // dim per 8 bytes) with key groups swizzled by dim; keys 0-63 of the step go to half
   // 0, keys 64-127 to half 1.
+  //
+  // Per-thread constants.  K chunk i of a thread is key kkey0 + KSTRIDE*i, chunk kch
+  // (KSTRIDE is a multiple of 16, so its row inside the block never changes).  The V
+  // task (vhalf, vkg, vj) loads chunk vj of keys 64*vhalf + 4*vkg + i, i < 4: one
+  // block (offset vblk in the step), rows 4*(vkg%4) + i.
+  constexpr int KSTRIDE = kPThreads / NCH;
+  static_assert(KSTRIDE % kBlock == 0, "K rows must stay fixed across a thread's chunks");
+  const uint32_t blk_bytes = (uint32_t)a.num_kv_heads * kBlock * D * 2;
+  const int kch = tid % NCH;
+  const int kkey0 = tid / NCH;
+  const char *kthr = reinterpret_cast<const char *>(kpool) +
+                     (((size_t)kvh * kBlock + kkey0 % kBlock) * D + kch * 8) * 2;
   uint4 kreg[KCH];
   uint4 vreg[4];
   const bool vtask = tid < 2 * VTH;
   const int vhalf = tid / VTH;
   const int vkg = tid & 15;
   const int vj = (tid % VTH) >> 4;
-#define PKV_KEY_ROW(pool, kidx)                                                          \
-  (reinterpret_cast<const uint4 *>(                                                      \
-      (pool) + (((size_t)s_tbl[((kidx) / kBlock) % kTblCache] * a.num_kv_heads + kvh) *  \
-                    kBlock + ((kidx) % kBlock)) * D))
+  const int vblk = 4 * vhalf + vkg / 4;
+  const char *vthr = reinterpret_cast<const char *>(vpool) +
+                     (((size_t)kvh * kBlock + 4 * (vkg % 4)) * D + vj * 8) * 2;
 #define PKV_FETCH(st)                                                                    \
   do {                                                                                   \
-    const int k0_ = (st) * kStepKeys;                                                    \
+    const int b0_ = ((st) * (kStepKeys / kBlock)) % kTblCache;                           \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const int c = tid + kPThreads * i;                                                 \
-      const int key = c / NCH;                                                           \
-      const int kidx = min(k0_ + key, kv_end - 1);                                       \
-      kreg[i] = PKV_KEY_ROW(kpool, kidx)[c - key * NCH];                                 \
+      const uint32_t blk_ = (uint32_t)s_tbl[b0_ + (kkey0 + KSTRIDE * i) / kBlock];       \
+      kreg[i] = *reinterpret_cast<const uint4 *>(kthr + (uint64_t)blk_ * blk_bytes);     \
     }                                                                                    \
     if (vtask) {                                                                         \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
-        const int kidx = min(k0_ + kHalfKeys * vhalf + 4 * vkg + i, kv_end - 1);         \
-        vreg[i] = PKV_KEY_ROW(vpool, kidx)[vj];                                          \
-      }                                                                                  \
+      const uint32_t blk_ = (uint32_t)s_tbl[b0_ + vblk];                                 \
+      const char *p_ = vthr + (uint64_t)blk_ * blk_bytes;                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
+        vreg[i] = *reinterpret_cast<const uint4 *>(p_ + i * D * 2);                      \
     }                                                                                    \
   } while (0)
-#define PKV_STAGE(st, buf)                                                               \
+  // Zero what lies past kv_end (only the last step has any).
+#define PKV_MASK_REGS(st)                                                                \
   do {                                                                                   \
     const int k0_ = (st) * kStepKeys;                                                    \
+    if (k0_ + kStepKeys > kv_end) {                                                      \
+      _Pragma("unroll") for (int i = 0; i < KCH; ++i) if (k0_ + kkey0 + KSTRIDE * i >=   \
+                                                            kv_end) kreg[i] = uint4{};   \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) if (k0_ + kHalfKeys * vhalf +        \
+                                                        4 * vkg + i >= kv_end)           \
+          vreg[i] = uint4{};                                                             \
+    }                                                                                    \
+  } while (0)
+#define PKV_STAGE(buf)                                                                   \
+  do {                                                                                   \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const int c = tid + kPThreads * i;                                                 \
-      const int key = c / NCH;                                                           \
-      const int ch = c - key * NCH;                                                      \
+      const int key = kkey0 + KSTRIDE * i;                                               \
       const int kh = key / kHalfKeys;                                                    \
       const int kl = key % kHalfKeys;                                                    \
-      const bool live = k0_ + key < kv_end;                                              \
-      const uint4 x = kreg[i];                                                           \
-      k_lds[((buf) * 2 + kh) * K_U4 + kl * NCH + (ch ^ (kl % NCH))] =                    \
-          uint4{live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u};     \
+      k_lds[((buf) * 2 + kh) * K_U4 + kl * NCH + (kch ^ (kl % NCH))] = kreg[i];          \
     }                                                                                    \
     if (vtask) {                                                                         \
-      uint32_t w[4][4];                                                                  \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
-        const bool live = k0_ + kHalfKeys * vhalf + 4 * vkg + i < kv_end;                \
-        w[i][0] = live ? vreg[i].x : 0u;                                                 \
-        w[i][1] = live ? vreg[i].y : 0u;                                                 \
-        w[i][2] = live ? vreg[i].z : 0u;                                                 \
-        w[i][3] = live ? vreg[i].w : 0u;                                                 \
-      }                                                                                  \
       uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2;                                  \
+      const uint32_t w_[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},           \
+                                 {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},           \
+                                 {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},           \
+                                 {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};          \
       _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
         const int d0 = 8 * vj + 2 * e;                                                   \
         const int d1 = d0 + 1;                                                           \
         vt_[d0 * 16 + (vkg ^ (d0 & 15))] =                                               \
-            uint2{(w[0][e] & 0xffffu) | (w[1][e] << 16),                                 \
-                  (w[2][e] & 0xffffu) | (w[3][e] << 16)};                                \
+            uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermLo),                    \
+                  __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermLo)};                   \
         vt_[d1 * 16 + (vkg ^ (d1 & 15))] =                                               \
-            uint2{(w[0][e] >> 16) | (w[1][e] & 0xffff0000u),                             \
-                  (w[2][e] >> 16) | (w[3][e] & 0xffff0000u)};                            \
+            uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermHi),                    \
+                  __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermHi)};                   \
       }                                                                                  \
     }                                                                                    \
   } while (0)
@@ -379,7 +395,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   __syncthreads();
   if (nst > 0) {
     PKV_FETCH(0);
-    PKV_STAGE(0, 0);
+    PKV_MASK_REGS(0);
+    PKV_STAGE(0);
   }
   __syncthreads();
   // Retire every outstanding load (the query fragments in particular) on all paths
@@ -409,7 +426,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         tile_update<D, false>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
                               l16, lg);
     }
-    if (st + 1 < nst) PKV_STAGE(st + 1, buf ^ 1);
+    if (st + 1 < nst) {
+      PKV_MASK_REGS(st + 1);
+      PKV_STAGE(buf ^ 1);
+    }
     __syncthreads();  // step st+1 staged; everyone is done reading step st
   }
 
@@ -461,8 +481,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 }
 
 #undef PKV_FILL_TBL
-#undef PKV_KEY_ROW
 #undef PKV_FETCH
+#undef PKV_MASK_REGS
 #undef PKV_STAGE
 
 template <int D, int HGP>
