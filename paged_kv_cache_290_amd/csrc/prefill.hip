@@ -65,7 +65,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) {
 }
 
 // One wave's update with a 64-key tile: kb = K tile [key][chunk ^ key%NCH], vb = V^T
-// tile [dim][keygroup ^ dim%16]; kbase = position of the tile's first key.  MASK
+// tile [dim][16-byte unit ^ dim%8] (two 4-key groups per unit); kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
 // position or past kv_end).
 template <int D, bool MASK>
@@ -162,14 +162,13 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint2 *vb,
 
   // O^T += V^T P^T: A row = dim, k-slots (lg, e) <-> keys 32*ks2 + 4*lg + e (e < 4)
   // and 32*ks2 + 16 + 4*lg + (e - 4), matching the slots of pf.
+  const uint4 *vb4 = reinterpret_cast<const uint4 *>(vb);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int dim = mt * 16 + l16;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const uint2 a0 = vb[dim * 16 + ((8 * ks2 + lg) ^ (dim & 15))];
-      const uint2 a1 = vb[dim * 16 + ((8 * ks2 + 4 + lg) ^ (dim & 15))];
-      const bf16x8_t af = as_bf16x8(uint4{a0.x, a0.y, a1.x, a1.y});
+      const bf16x8_t af = as_bf16x8(vb4[dim * 8 + ((4 * ks2 + lg) ^ (dim & 7))]);
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) o[mt][cg] = mfma16(af, pf[cg][ks2], o[mt][cg]);
     }
@@ -187,7 +186,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
   constexpr int NCH = D / 8;        // 16-byte chunks per K row
   constexpr int K_U4 = kHalfKeys * NCH;               // uint4 per K tile
-  constexpr int V_U2 = D * (kHalfKeys / 4);           // uint2 per V^T tile
+  constexpr int V_U2 = D * (kHalfKeys / 4);           // uint2 per V^T tile (4 keys each)
   constexpr int KCH = kStepKeys * NCH / kPThreads;    // K chunks per thread per step
   constexpr int VTH = 16 * NCH;                       // (4-key group, chunk) tasks per half
   constexpr int LDS_U4 = 4 * K_U4 + 2 * V_U2;         // [buf][half] K tiles, then V^T
@@ -315,8 +314,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   // is past the sequence (the cache holds 0 there), and is zeroed when staged, so all
   // of a step's loads leave back to back.  stage: registers -> LDS buffer `buf`: K
   // row-major with the chunk index XOR-swizzled by key, V transposed (4 keys of one
-  // dim per 8 bytes) with key groups swizzled by dim; keys 0-63 of the step go to half
-  // 0, keys 64-127 to half 1.
+  // dim per 8 bytes) in 16-byte units of two key groups swizzled by dim; keys 0-63 of
+  // the step go to half 0, keys 64-127 to half 1.
   //
   // Per-thread constants.  K chunk i of a thread is key kkey0 + KSTRIDE*i, chunk kch
   // (KSTRIDE is a multiple of 16, so its row inside the block never changes).  The V
@@ -336,6 +335,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int vkg = tid & 15;
   const int vj = (tid % VTH) >> 4;
   const int vblk = 4 * vhalf + vkg / 4;
+  // V^T row slot of this task's key group: key groups 8*k2 + 4*h + g (k2, h < 2,
+  // g < 4) pair up as 16-byte unit 4*k2 + g, half h, so each MFMA A fragment (keys
+  // 32*k2 + 4*g + 0..3 and 32*k2 + 16 + 4*g + 0..3) is one 16-byte read.
+  const int vpair = 4 * (vkg / 8) + (vkg % 4);
+  const int vpair_h = (vkg / 4) % 2;
   const char *vthr = reinterpret_cast<const char *>(vpool) +
                      (((size_t)kvh * kBlock + 4 * (vkg % 4)) * D + vj * 8) * 2;
 #define PKV_FETCH(st)                                                                    \
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       k_lds[((buf) * 2 + kh) * K_U4 + kl * NCH + (kch ^ (kl % NCH))] = kreg[i];          \
     }                                                                                    \
     if (vtask) {                                                                         \
-      uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2;                                  \
+      uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2 + vpair_h;                        \
       const uint32_t w_[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},           \
                                  {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},           \
                                  {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},           \
@@ -381,10 +385,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
         const int d0 = 8 * vj + 2 * e;                                                   \
         const int d1 = d0 + 1;                                                           \
-        vt_[d0 * 16 + (vkg ^ (d0 & 15))] =                                               \
+        vt_[d0 * 16 + 2 * (vpair ^ (d0 & 7))] =                                          \
             uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermLo),                    \
                   __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermLo)};                   \
-        vt_[d1 * 16 + (vkg ^ (d1 & 15))] =                                               \
+        vt_[d1 * 16 + 2 * (vpair ^ (d1 & 7))] =                                          \
             uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermHi),                    \
                   __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermHi)};                   \
       }                                                                                  \
