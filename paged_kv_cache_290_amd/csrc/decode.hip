@@ -72,6 +72,21 @@ __device__ __forceinline__ float sum_over_chunk_lanes(float x) {
   return x;
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  x += shfl_xor(x, 16);
+  x += shfl_xor(x, 32);
+  return x;
+}
+
+// v_perm_b32 selectors: (s0, s1) -> (s1.lo16, s0.lo16) and (s1.hi16, s0.hi16) (selector
+// bytes 0-3 pick bytes of the second operand, 4-7 of the first).
+constexpr uint32_t kPermLo = 0x05040100u;
+constexpr uint32_t kPermHi = 0x07060302u;
+
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kQuadSwap1>(x));
   x = fmaxf(x, dpp<kQuadSwap2>(x));
@@ -106,20 +121,24 @@ __device__ __forceinline__ bool item_row(const AttnArgs &a, int item, int &seq, 
 }
 
 // Per-item block counts -> exclusive prefix in LDS (s_pref[0..items], s_pref[items] =
-// total), visible keys in s_keys.  Whole workgroup; ends with a barrier.
+// total), visible keys in s_keys, query row and sequence in s_row / s_seq.  Whole
+// workgroup; ends with a barrier.
 template <bool kRows>
 __device__ __forceinline__ void scan_items(const AttnArgs &a, int base, int items,
-                                           int *s_pref, int *s_keys, int *s_tmp) {
+                                           int *s_pref, int *s_keys, int *s_row, int *s_seq,
+                                           int *s_tmp) {
   const int tid = threadIdx.x;
   const int per = (items + kThreads - 1) / kThreads;
   const int i0 = min(items, tid * per);
   const int i1 = min(items, i0 + per);
   int local = 0;
   for (int i = i0; i < i1; ++i) {
-    int seq, row, keys;
+    int seq = 0, row = 0, keys;
     bool zero;
     if (!item_row<kRows>(a, base + i, seq, row, keys, zero)) keys = 0;
     s_keys[i] = keys;
+    s_row[i] = row;
+    s_seq[i] = seq;
     const int n = (keys + kBlock - 1) / kBlock;
     s_pref[i] = n;
     local += n;
@@ -162,9 +181,17 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
 
   __shared__ int s_pref[kMaxStreamItems + 1];
   __shared__ int s_keys[kMaxStreamItems];
+  __shared__ int s_row[kMaxStreamItems];
+  __shared__ int s_seq[kMaxStreamItems];
   __shared__ int s_tmp[kThreads];
+  // bf16 path: per wave and ring slot, partial scores [j*HG + hh][lane] and the bf16
+  // weights [token group][head][j] exchanged between the lanes of the wave.
+  constexpr int kRed = kF32 ? 1 : NV * HG * 64;
+  constexpr int kPw = kF32 ? 1 : 16 * HG / 2;
+  __shared__ float s_red[kWaves][PF + 1][kRed];
+  __shared__ uint32_t s_pw[kWaves][PF + 1][kPw];
 
-  scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_tmp);
+  scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_row, s_seq, s_tmp);
   const int rows_total = s_pref[p.items];
   const int64_t T_all = (int64_t)rows_total * p.groups;
   // With fewer blocks than waves only the first T_all waves work, so every working
@@ -207,191 +234,65 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
   const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (w >= W) return;
-  int64_t b = (int64_t)w * T_all / W;
-  const int64_t b_end = (int64_t)(w + 1) * T_all / W;
+  const int64_t wb0 = (int64_t)w * T_all / W;  // the wave's blocks: [wb0, wb0 + nbw)
+  const int nbw = (int)((int64_t)(w + 1) * T_all / W - wb0);
   const int group = a.num_q_heads / a.num_kv_heads;
   const char *kpool = static_cast<const char *>(a.k_pool);
   const char *vpool = static_cast<const char *>(a.v_pool);
 
-  while (b < b_end) {
-    // ---- locate the piece: group g, item, first logical block, block count ----
-    const int g = (int)(b / rows_total);
-    const int r = (int)(b - (int64_t)g * rows_total);
-    int lo = 0, hi = p.items - 1;  // last item with s_pref[item] <= r
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= r) lo = mid; else hi = mid - 1;
-    }
-    const int item = lo;
-    const int lb0 = r - s_pref[item];
-    const int n_item = s_pref[item + 1] - s_pref[item];
-    const int n = (int)min<int64_t>(n_item - lb0, b_end - b);
-    const bool whole = lb0 == 0 && n == n_item;
-    const int seg = g * p.items + item;
-    b += n;
+  // bf16: after the exchange lane `lane` < NSC owns the score of token tau_s (of the
+  // current block) and head hh_s.  The softmax scale enters as |scale| with the sign
+  // of a negative scale folded into q (exact for bf16).
+  constexpr int NSC = 16 * HG;
+  const int k_s = lane / TPI;
+  const int j_s = k_s / HG;
+  const int hh_s = k_s - j_s * HG;
+  const int tau_s = TPI * j_s + (lane - k_s * TPI);
+  const bool scoring = lane < NSC;
+  const float sc = fabsf(a.scale_log2);
+  const uint32_t qflip = (!kF32 && a.scale_log2 < 0.f) ? 0x80008000u : 0u;
 
-    int seq, row, keys;
-    bool zero;
-    item_row<kF32>(a, p.item_base + item, seq, row, keys, zero);
+  // State of the open piece (the wave's blocks of one segment).
+  uint32_t qw[HG][WPC];  // its query fragment: this lane's EPC dims of each head
+  uint32_t qn[HG][WPC];  // query fragment prefetched for the next piece
+  int qn_block = -1;     // wave block at which that next piece starts
+  float acc[HG][EPC];
+  float lsum[HG];   // fp32: per head, over this lane's tokens
+  float mref[HG];   // reference max per head (wave-uniform)
+  float my_m = -INFINITY;  // bf16: mref of this lane's score head
+  float my_l = 0.f;        // bf16: this lane's share of its head's weight sum
+  bool pc_open = false, pc_whole = false;
+  int pc_row = 0, pc_h0 = 0, pc_keys = 0, pc_seg = 0;
+
+  auto load_q = [&](uint32_t (&dst)[HG][WPC], int row, int h0) {
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
+                  chunk * EPC;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
+      dst[hh][0] = x.x ^ qflip; dst[hh][1] = x.y ^ qflip;
+      dst[hh][2] = x.z ^ qflip; dst[hh][3] = x.w ^ qflip;
+    }
+  };
+  auto head0 = [&](int g) {
     const int kvh = g / p.num_head_groups;
-    const int h0 = kvh * group + (g - kvh * p.num_head_groups) * HG;
+    return kvh * group + (g - kvh * p.num_head_groups) * HG;
+  };
 
-    // ---- query fragment: this lane's EPC dims (chunk) of each of the HG heads ----
-    uint32_t qw[HG][WPC];
-    {
-      const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
-                    chunk * EPC;
+  // Totals of the open piece: the whole segment goes straight to `out`, a part of one
+  // to its partial slot (normalised o and log2-sum-exp per head).
+  auto flush = [&]() {
+    if constexpr (!kF32) {
+      // bf16: the weight sum of head hh is spread over the lanes that scored it.
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
-        qw[hh][0] = x.x; qw[hh][1] = x.y; qw[hh][2] = x.z; qw[hh][3] = x.w;
-        if constexpr (kF32) {  // fold the softmax scale into q once
-#pragma unroll
-          for (int k = 0; k < WPC; ++k)
-            qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
-        }
-      }
+      for (int hh = 0; hh < HG; ++hh) lsum[hh] = wave_sum((scoring && hh_s == hh) ? my_l : 0.f);
     }
-
-    float acc[HG][EPC];
-    float lsum[HG];
-    float mref[HG];
+    // fp32: each token's weight was counted on all CPR lanes of the token; summing over
+    // the lanes of one chunk (one per token group) gives the piece's totals.  The
+    // accumulators of both paths hold one chunk's dims per lane and token group.
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      lsum[hh] = 0.f;
-      mref[hh] = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
-    }
-
-    const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-      const int nc = min(64, n - c0);
-      // Physical block ids of this chunk of the piece: lane i holds the i-th.
-      const int my_pb = lane < nc ? tbl[c0 + lane] : 0;
-      const int lb_first = lb0 + c0;
-
-      // Raw buffer loads through a per-tile descriptor.  Prefetches past the chunk (and
-      // tiles of invalid table entries) get a descriptor with no records: those loads
-      // fetch nothing and return zeros, yet every path issues the same number of
-      // loads, so the compiler's wait counts stay exact.
-      auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
-        int pb = readlane(my_pb, min(i, nc - 1));
-        const bool ok = i < nc && pb >= 0 && pb < a.num_blocks;
-        pb = ok ? pb : 0;
-        const size_t off = ((size_t)pb * a.num_kv_heads + kvh) * kTileBytes;
-        const int nrec = ok ? kTileBytes : 0;
-        const buffer_rsrc_t rk = make_rsrc(kpool + off, nrec);
-        const buffer_rsrc_t rv = make_rsrc(vpool + off, nrec);
-#pragma unroll
-        for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
-#pragma unroll
-        for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
-      };
-      auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
-        const int lb = lb_first + i;
-        const int pb = readlane(my_pb, i);
-        const bool bad = pb < 0 || pb >= a.num_blocks;
-        const int key0 = lb * kBlock + tok0;
-        float s[NV][HG];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
-#pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            float x = 0.f;
-#pragma unroll
-            for (int k = 0; k < WPC; ++k) {
-              if constexpr (kF32)
-                x = fmaf(__uint_as_float(qw[hh][k]), __uint_as_float(kw[k]), x);
-              else
-                x = dot2_bf16(qw[hh][k], kw[k], x);
-            }
-            s[j][hh] = x;
-          }
-        }
-        bool need = false;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const bool valid = !bad && (key0 + TPI * j) < keys;
-#pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            float x = sum_over_token_lanes<CPR>(s[j][hh]);
-            if constexpr (!kF32) x *= a.scale_log2;
-            x = valid ? x : -INFINITY;
-            s[j][hh] = x;
-            need |= x > mref[hh] + kRescaleSlack;
-          }
-        }
-        if (wave_any(need)) {
-#pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            float mx = s[0][hh];
-#pragma unroll
-            for (int j = 1; j < NV; ++j) mx = fmaxf(mx, s[j][hh]);
-            const float mn = fmaxf(mref[hh], wave_max(mx));
-            const float alpha = (mref[hh] == -INFINITY) ? 0.f : fast_exp2(mref[hh] - mn);
-            mref[hh] = mn;
-            lsum[hh] *= alpha;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha;
-          }
-        }
-        // Slots past the context (and tiles of invalid blocks) may hold anything,
-        // including NaN: their weight is 0 and their values are replaced by 0.
-        const bool edge = bad || (lb + 1) * kBlock > keys;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const bool valid = !bad && (key0 + TPI * j) < keys;
-          uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-          if (edge) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) vw[k] = valid ? vw[k] : 0u;
-          }
-          float pr[HG];
-#pragma unroll
-          for (int hh = 0; hh < HG; ++hh) {
-            pr[hh] = valid ? fast_exp2(s[j][hh] - mref[hh]) : 0.f;
-            lsum[hh] += pr[hh];
-          }
-#pragma unroll
-          for (int k = 0; k < WPC; ++k) {
-            if constexpr (kF32) {
-              const float x = __uint_as_float(vw[k]);
-#pragma unroll
-              for (int hh = 0; hh < HG; ++hh) acc[hh][k] = fmaf(pr[hh], x, acc[hh][k]);
-            } else {
-              const float lo = bf16_lo(vw[k]);
-              const float hi = bf16_hi(vw[k]);
-#pragma unroll
-              for (int hh = 0; hh < HG; ++hh) {
-                acc[hh][2 * k] = fmaf(pr[hh], lo, acc[hh][2 * k]);
-                acc[hh][2 * k + 1] = fmaf(pr[hh], hi, acc[hh][2 * k + 1]);
-              }
-            }
-          }
-        }
-      };
-
-      // Ring of PF+1 register buffers: while block i is computed, blocks i+1..i+PF
-      // are in flight.
-      uint4 kb[PF + 1][NV], vb[PF + 1][NV];
-#pragma unroll
-      for (int q = 0; q < PF; ++q) load(kb[q], vb[q], q);
-      for (int i0 = 0; i0 < nc; i0 += PF + 1) {
-#pragma unroll
-        for (int u = 0; u <= PF; ++u) {
-          load(kb[(u + PF) % (PF + 1)], vb[(u + PF) % (PF + 1)], i0 + u + PF);
-          if (i0 + u < nc) compute(kb[u], vb[u], i0 + u);
-        }
-      }
-    }
-
-    // Each token's weight was counted on all CPR lanes of the token; summing over the
-    // lanes of one chunk (one per token group) gives the piece's totals for that chunk.
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
+      if constexpr (kF32) lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
     }
@@ -399,9 +300,9 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
         const float inv = lsum[hh] > 0.f ? 1.f / lsum[hh] : 0.f;
-        if (whole) {
-          T *dst = static_cast<T *>(a.out) + ((size_t)row * a.num_q_heads + h0 + hh) * D +
-                   chunk * EPC;
+        if (pc_whole) {
+          T *dst = static_cast<T *>(a.out) +
+                   ((size_t)pc_row * a.num_q_heads + pc_h0 + hh) * D + chunk * EPC;
           if constexpr (kF32) {
             *reinterpret_cast<float4 *>(dst) =
                 float4{acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv};
@@ -414,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
             *reinterpret_cast<uint4 *>(dst) = pk;
           }
         } else {
-          const size_t slot = (size_t)(seg + w) * HG + hh;
+          const size_t slot = (size_t)(pc_seg + w) * HG + hh;
           float *dst = p.ws_o + slot * D + chunk * EPC;
 #pragma unroll
           for (int e = 0; e < EPC; e += 4)
@@ -427,7 +328,298 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
         }
       }
     }
+  };
+
+  for (int c0 = 0; c0 < nbw; c0 += 64) {
+    const int nc = min(64, nbw - c0);
+    // Lane i describes wave block c0 + i: its kv-head group g, item, logical block and
+    // physical block (invalid table entries read block 0 and are masked).  All table
+    // entries of the chunk are fetched at once, whatever pieces the chunk spans.
+    int m_g = 0, m_item = 0, m_lb = 0, m_pb = 0, m_ok = 0;
+    if (lane < nc) {
+      const int64_t bi = wb0 + c0 + lane;
+      m_g = (int)(bi / rows_total);
+      const int r = (int)(bi - (int64_t)m_g * rows_total);
+      int lo = 0, hi = p.items - 1;  // last item with s_pref[item] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      m_item = lo;
+      m_lb = r - s_pref[lo];
+      const int pb = a.block_tables[(size_t)s_seq[lo] * a.max_blocks_per_seq + m_lb];
+      m_ok = pb >= 0 && pb < a.num_blocks;
+      m_pb = m_ok ? pb : 0;
+    }
+    // Pieces start at a segment's first block, and at the wave's first block.
+    uint64_t starts = __builtin_amdgcn_ballot_w64(lane < nc && m_lb == 0);
+    if (c0 == 0) starts |= 1ull;
+
+    // Raw buffer loads through a per-tile descriptor.  Prefetches past the chunk (and
+    // tiles of invalid table entries) get a descriptor with no records: those loads
+    // fetch nothing and return zeros, yet every path issues the same number of
+    // loads, so the compiler's wait counts stay exact.
+    auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
+      const int ic = min(i, nc - 1);
+      const int pb = readlane(m_pb, ic);
+      const bool ok = i < nc && readlane(m_ok, ic) != 0;
+      const int kvh = readlane(m_g, ic) / p.num_head_groups;
+      const size_t off = ((size_t)pb * a.num_kv_heads + kvh) * kTileBytes;
+      const int nrec = ok ? kTileBytes : 0;
+      const buffer_rsrc_t rk = make_rsrc(kpool + off, nrec);
+      const buffer_rsrc_t rv = make_rsrc(vpool + off, nrec);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
+    };
+
+    // A new piece at chunk block i: flush the open one, set up the new one, and
+    // prefetch the query of the piece after it (if that one starts in this chunk).
+    auto begin_piece = [&](int i) {
+      if (pc_open) flush();
+      const int g = readlane(m_g, i);
+      const int item = readlane(m_item, i);
+      const int lb0 = readlane(m_lb, i);
+      pc_row = s_row[item];
+      pc_keys = s_keys[item];
+      pc_h0 = head0(g);
+      pc_seg = g * p.items + item;
+      const int n_item = s_pref[item + 1] - s_pref[item];
+      const int len = min(n_item - lb0, nbw - (c0 + i));
+      pc_whole = lb0 == 0 && len == n_item;
+      pc_open = true;
+      if (qn_block == c0 + i) {
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+          for (int k = 0; k < WPC; ++k) qw[hh][k] = qn[hh][k];
+      } else {
+        load_q(qw, pc_row, pc_h0);
+      }
+      if constexpr (kF32) {  // fold the softmax scale into q once
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+          for (int k = 0; k < WPC; ++k)
+            qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
+      }
+      const uint64_t later = i < 63 ? starts & (~0ull << (i + 1)) : 0ull;
+      if (later) {
+        const int j = __builtin_ctzll(later);
+        const int gj = readlane(m_g, j);
+        load_q(qn, s_row[readlane(m_item, j)], head0(gj));
+        qn_block = c0 + j;
+      }
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        lsum[hh] = 0.f;
+        mref[hh] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+      }
+      my_m = -INFINITY;
+      my_l = 0.f;
+    };
+
+    // bf16 block update.  Each lane forms the partial dot products of its chunk for
+    // its NV tokens and HG heads and parks them in LDS; lane `lane` < NSC then adds the
+    // CPR partials of one (token, head) score, so the softmax work (scale, mask, exp)
+    // is done once per score.  The weights go back through LDS as bf16, laid out so a
+    // lane reads its token pairs as packed words and P.V is one dot2 per (head, dim,
+    // token pair).  The denominator sums the same rounded weights.
+    auto compute_bf16 = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i, int u) {
+      const int lb = readlane(m_lb, i);
+      const bool bad = readlane(m_ok, i) == 0;
+      const int keys = pc_keys;
+      float *red = s_red[wave][u];
+      uint32_t *pw = s_pw[wave][u];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          float x = 0.f;
+#pragma unroll
+          for (int k = 0; k < WPC; ++k) x = dot2_bf16(qw[hh][k], kw[k], x);
+          red[(j * HG + hh) * 64 + lane] = x;
+        }
+      }
+      float xs = -INFINITY;
+      if (scoring) {
+        const float4 *src = reinterpret_cast<const float4 *>(red + lane * CPR);
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPR / 4; ++c) {
+          const float4 v4 = src[c];
+          x += (v4.x + v4.y) + (v4.z + v4.w);
+        }
+        if (!bad && lb * kBlock + tau_s < keys) xs = x * sc;
+      }
+      if (wave_any(xs > my_m + kRescaleSlack)) {
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          const float mn = fmaxf(mref[hh], wave_max(hh_s == hh ? xs : -INFINITY));
+          const float alpha = (mref[hh] == -INFINITY) ? 0.f : fast_exp2(mref[hh] - mn);
+          mref[hh] = mn;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha;
+          if (hh_s == hh) {
+            my_l *= alpha;
+            my_m = mn;
+          }
+        }
+      }
+      if (scoring) {
+        const float pr = (xs == -INFINITY) ? 0.f : fast_exp2(xs - my_m);
+        const uint16_t pb = f32_to_bf16(pr);
+        my_l += __uint_as_float((uint32_t)pb << 16);
+        reinterpret_cast<uint16_t *>(pw)[((tau_s % TPI) * HG + hh_s) * NV + tau_s / TPI] = pb;
+      }
+      // Slots past the context (and tiles of invalid blocks) may hold anything,
+      // including NaN: their weight is 0 and their values are replaced by 0.
+      const bool edge = bad || (lb + 1) * kBlock > keys;
+      uint32_t vw[NV][4];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        vw[j][0] = vr[j].x; vw[j][1] = vr[j].y; vw[j][2] = vr[j].z; vw[j][3] = vr[j].w;
+        if (edge) {
+          const bool valid = !bad && lb * kBlock + TPI * j + tok0 < keys;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vw[j][k] = valid ? vw[j][k] : 0u;
+        }
+      }
+      // Weights of this lane's tokens: word (hh, jp) = (p[TPI*2jp + tok0], p[TPI*(2jp+1)
+      // + tok0]) of head hh.
+      uint32_t pp[HG][NV / 2];
+      {
+        const uint32_t *src = pw + tok0 * (HG * NV / 2);
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+          for (int jp = 0; jp < NV / 2; ++jp) pp[hh][jp] = src[hh * (NV / 2) + jp];
+      }
+#pragma unroll
+      for (int jp = 0; jp < NV / 2; ++jp) {
+#pragma unroll
+        for (int k = 0; k < WPC; ++k) {
+          const uint32_t lo = __builtin_amdgcn_perm(vw[2 * jp + 1][k], vw[2 * jp][k], kPermLo);
+          const uint32_t hi = __builtin_amdgcn_perm(vw[2 * jp + 1][k], vw[2 * jp][k], kPermHi);
+#pragma unroll
+          for (int hh = 0; hh < HG; ++hh) {
+            acc[hh][2 * k] = dot2_bf16(pp[hh][jp], lo, acc[hh][2 * k]);
+            acc[hh][2 * k + 1] = dot2_bf16(pp[hh][jp], hi, acc[hh][2 * k + 1]);
+          }
+        }
+      }
+    };
+
+    auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
+      const int lb = readlane(m_lb, i);
+      const bool bad = readlane(m_ok, i) == 0;
+      const int key0 = lb * kBlock + tok0;
+      const int keys = pc_keys;
+      float s[NV][HG];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          float x = 0.f;
+#pragma unroll
+          for (int k = 0; k < WPC; ++k) {
+            if constexpr (kF32)
+              x = fmaf(__uint_as_float(qw[hh][k]), __uint_as_float(kw[k]), x);
+            else
+              x = dot2_bf16(qw[hh][k], kw[k], x);
+          }
+          s[j][hh] = x;
+        }
+      }
+      bool need = false;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool valid = !bad && (key0 + TPI * j) < keys;
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          float x = sum_over_token_lanes<CPR>(s[j][hh]);
+          if constexpr (!kF32) x *= a.scale_log2;
+          x = valid ? x : -INFINITY;
+          s[j][hh] = x;
+          need |= x > mref[hh] + kRescaleSlack;
+        }
+      }
+      if (wave_any(need)) {
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          float mx = s[0][hh];
+#pragma unroll
+          for (int j = 1; j < NV; ++j) mx = fmaxf(mx, s[j][hh]);
+          const float mn = fmaxf(mref[hh], wave_max(mx));
+          const float alpha = (mref[hh] == -INFINITY) ? 0.f : fast_exp2(mref[hh] - mn);
+          mref[hh] = mn;
+          lsum[hh] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[hh][e] *= alpha;
+        }
+      }
+      // Slots past the context (and tiles of invalid blocks) may hold anything,
+      // including NaN: their weight is 0 and their values are replaced by 0.
+      const bool edge = bad || (lb + 1) * kBlock > keys;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool valid = !bad && (key0 + TPI * j) < keys;
+        uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+        if (edge) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vw[k] = valid ? vw[k] : 0u;
+        }
+        float pr[HG];
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          pr[hh] = valid ? fast_exp2(s[j][hh] - mref[hh]) : 0.f;
+          lsum[hh] += pr[hh];
+        }
+#pragma unroll
+        for (int k = 0; k < WPC; ++k) {
+          if constexpr (kF32) {
+            const float x = __uint_as_float(vw[k]);
+#pragma unroll
+            for (int hh = 0; hh < HG; ++hh) acc[hh][k] = fmaf(pr[hh], x, acc[hh][k]);
+          } else {
+            const float lo = bf16_lo(vw[k]);
+            const float hi = bf16_hi(vw[k]);
+#pragma unroll
+            for (int hh = 0; hh < HG; ++hh) {
+              acc[hh][2 * k] = fmaf(pr[hh], lo, acc[hh][2 * k]);
+              acc[hh][2 * k + 1] = fmaf(pr[hh], hi, acc[hh][2 * k + 1]);
+            }
+          }
+        }
+      }
+    };
+
+    // Ring of PF+1 register buffers: while block i is computed, blocks i+1..i+PF are
+    // in flight, across piece boundaries.
+    uint4 kb[PF + 1][NV], vb[PF + 1][NV];
+#pragma unroll
+    for (int q = 0; q < PF; ++q) load(kb[q], vb[q], q);
+    for (int i0 = 0; i0 < nc; i0 += PF + 1) {
+#pragma unroll
+      for (int u = 0; u <= PF; ++u) {
+        load(kb[(u + PF) % (PF + 1)], vb[(u + PF) % (PF + 1)], i0 + u + PF);
+        const int i = i0 + u;
+        if (i < nc) {
+          if ((starts >> i) & 1ull) begin_piece(i);
+          if constexpr (kF32)
+            compute(kb[u], vb[u], i);
+          else
+            compute_bf16(kb[u], vb[u], i, u);
+        }
+      }
+    }
   }
+  if (pc_open) flush();
 }
 
 // Log-sum-exp merge of the pieces of each segment cut across waves: with per-piece
