@@ -125,6 +125,31 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
                                   int32_t block_size, float scale, pkv_dtype dtype,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * paged_attention_varlen_with_write -- one launch sequence for a whole step: the slot
+ * write of this step's new rows and the attention over the updated pools.
+ * (Same passages as paged_kv_write and paged_attention_varlen; the inference-engine
+ * page's KV-cache section: each step appends its new tokens' K/V, then attends.)
+ *
+ * The result (out and both pools) is the same as paged_kv_write(k_new, v_new, k_pool,
+ * v_pool, slot_mapping, total_q, ...) followed by paged_attention_varlen(...) with the
+ * same arguments, under one extra precondition: new row t (a query row, [total_q]) is
+ * the token at position context_len - q_len + i of its sequence (i its index among the
+ * sequence's rows), and slot_mapping[t] is that position's table slot
+ * (block_tables[s][pos / 16] * 16 + pos % 16).  With that, bf16 single-token rows
+ * read their newest key and value straight from k_new / v_new while the same kernel
+ * stores all new rows, saving the separate write launch.  Other cases run the write
+ * kernel first.  Arguments as for the two calls above (k_new, v_new [total_q][Hkv][D]).
+ */
+pkv_status paged_attention_varlen_with_write(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *pkv_status_string(pkv_status status);
 

@@ -27,6 +27,11 @@ SIGNATURES = {
     "paged_attention_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _f32, ctypes.c_int, _vp, _sz, _vp]),
+    "paged_attention_varlen_with_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                         _vp, _vp, _vp, _i32, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _i32,
+                                                         _i32, _i32, _f32, ctypes.c_int,
+                                                         _vp, _sz, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),

@@ -118,16 +118,21 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t
       .ws_bytes;
 }
 
-pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
-                                  const void *v_pool, const int32_t *block_tables,
-                                  const int32_t *context_lens,
-                                  const int32_t *query_start_loc, int32_t num_seqs,
-                                  int32_t total_q, int32_t num_blocks,
-                                  int32_t max_blocks_per_seq, int32_t max_context_len,
-                                  int32_t max_query_len, int32_t num_q_heads,
-                                  int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t block_size, float scale, pkv_dtype dtype,
-                                  void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two attention entry points.  k_new / v_new / slot_mapping are
+// null for the plain call; for the fused call they carry this step's new rows.
+pkv_status attention_impl(void *out, const void *q, const void *k_new, const void *v_new,
+                          const void *k_pool, const void *v_pool,
+                          const int32_t *slot_mapping, const int32_t *block_tables,
+                          const int32_t *context_lens, const int32_t *query_start_loc,
+                          int32_t num_seqs, int32_t total_q, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                          int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, float scale, pkv_dtype dtype,
+                          void *workspace, size_t workspace_bytes, void *stream) {
   if (!dtype_ok(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
     return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q < 0 || num_blocks <= 0 || num_q_heads <= 0 ||
@@ -139,6 +144,8 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens ||
       !query_start_loc)
     return PKV_ERR_INVALID_ARG;
+  const bool with_write = k_new != nullptr;
+  if (with_write && (!v_new || !slot_mapping)) return PKV_ERR_INVALID_ARG;
 
   DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                 max_context_len, dtype);
@@ -170,9 +177,59 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
   const bool chunks = dtype == PKV_BF16 && max_query_len > 1;
   const bool decode_rows = !(chunks && num_seqs == 1 && total_q > 1);
   hipError_t e = hipSuccess;
-  if (decode_rows) e = launch_decode(a, plan, dtype, st);
+  if (with_write) {
+    if (dtype == PKV_BF16 && decode_rows) {
+      // The bf16 decode kernel stores the new rows itself and reads each decode row's
+      // newest key/value from k_new / v_new; the chunk kernel runs after it.
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.slot_mapping = slot_mapping;
+    } else {
+      e = launch_kv_write(k_new, v_new, const_cast<void *>(k_pool),
+                          const_cast<void *>(v_pool), slot_mapping, total_q, num_blocks,
+                          num_kv_heads, head_dim, dtype, st);
+    }
+  }
+  if (e == hipSuccess && decode_rows) e = launch_decode(a, plan, dtype, st);
   if (e == hipSuccess && chunks) e = launch_prefill(a, dtype, st);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *block_tables,
+                                  const int32_t *context_lens,
+                                  const int32_t *query_start_loc, int32_t num_seqs,
+                                  int32_t total_q, int32_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, float scale, pkv_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  return attention_impl(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, block_tables,
+                        context_lens, query_start_loc, num_seqs, total_q, num_blocks,
+                        max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
+                        num_kv_heads, head_dim, block_size, scale, dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+pkv_status paged_attention_varlen_with_write(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  return attention_impl(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                        context_lens, query_start_loc, num_seqs, total_q, num_blocks,
+                        max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
+                        num_kv_heads, head_dim, block_size, scale, dtype, workspace,
+                        workspace_bytes, stream);
 }
 
 pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,

@@ -191,6 +191,29 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   __shared__ float s_red[kWaves][PF + 1][kRed];
   __shared__ uint32_t s_pw[kWaves][PF + 1][kPw];
 
+  if (a.k_new != nullptr && p.item_base == 0) {
+    // Fused slot write of every new row (16-byte pieces spread over the grid); its
+    // latency overlaps the item scan.  Nothing in this launch reads those slots.
+    constexpr int kRowVecs = D * (int)sizeof(T) / 16;
+    const int64_t total = (int64_t)a.total_q * a.num_kv_heads * kRowVecs;
+    const int64_t per_token = (int64_t)a.num_kv_heads * kRowVecs;
+    const int64_t num_slots = (int64_t)a.num_blocks * kBlock;
+    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * kThreads) {
+      const int64_t t = idx / per_token;
+      const int rem = (int)(idx - t * per_token);
+      const int h = rem / kRowVecs;
+      const int piece = rem - h * kRowVecs;
+      const uint4 kx = static_cast<const uint4 *>(a.k_new)[idx];
+      const uint4 vx = static_cast<const uint4 *>(a.v_new)[idx];
+      const int64_t slot = a.slot_mapping[t];
+      if (slot < 0 || slot >= num_slots) continue;
+      const int64_t dst = ((slot / kBlock * a.num_kv_heads + h) * kBlock + slot % kBlock) *
+                              kRowVecs + piece;
+      static_cast<uint4 *>(const_cast<void *>(a.k_pool))[dst] = kx;
+      static_cast<uint4 *>(const_cast<void *>(a.v_pool))[dst] = vx;
+    }
+  }
   scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_row, s_seq, s_tmp);
   const int rows_total = s_pref[p.items];
   const int64_t T_all = (int64_t)rows_total * p.groups;
@@ -239,6 +262,9 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   const int group = a.num_q_heads / a.num_kv_heads;
   const char *kpool = static_cast<const char *>(a.k_pool);
   const char *vpool = static_cast<const char *>(a.v_pool);
+  const bool fused = !kF32 && a.k_new != nullptr;
+  const char *knew = static_cast<const char *>(a.k_new);
+  const char *vnew = static_cast<const char *>(a.v_new);
 
   // bf16: after the exchange lane `lane` < NSC owns the score of token tau_s (of the
   // current block) and head hh_s.  The softmax scale enters as |scale| with the sign
@@ -335,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
     // Lane i describes wave block c0 + i: its kv-head group g, item, logical block and
     // physical block (invalid table entries read block 0 and are masked).  All table
     // entries of the chunk are fetched at once, whatever pieces the chunk spans.
-    int m_g = 0, m_item = 0, m_lb = 0, m_pb = 0, m_ok = 0;
+    int m_g = 0, m_item = 0, m_lb = 0, m_pb = 0, m_ok = 0, m_keys = 0;
     if (lane < nc) {
       const int64_t bi = wb0 + c0 + lane;
       m_g = (int)(bi / rows_total);
@@ -347,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       }
       m_item = lo;
       m_lb = r - s_pref[lo];
+      m_keys = s_keys[lo];
       const int pb = a.block_tables[(size_t)s_seq[lo] * a.max_blocks_per_seq + m_lb];
       m_ok = pb >= 0 && pb < a.num_blocks;
       m_pb = m_ok ? pb : 0;
@@ -359,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
     // tiles of invalid table entries) get a descriptor with no records: those loads
     // fetch nothing and return zeros, yet every path issues the same number of
     // loads, so the compiler's wait counts stay exact.
-    auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
+    auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], uint4 &kn, uint4 &vn, int i) {
       const int ic = min(i, nc - 1);
       const int pb = readlane(m_pb, ic);
       const bool ok = i < nc && readlane(m_ok, ic) != 0;
@@ -372,6 +399,22 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
 #pragma unroll
       for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
+      if constexpr (!kF32) {
+        // Fused write: the lanes of a decode row's newest token (in its last block) also
+        // fetch that row from k_new / v_new; every other lane's offset is out of range,
+        // so the load fetches nothing (issued on every block to keep wait counts exact).
+        const int keys = readlane(m_keys, ic);
+        const int lb = readlane(m_lb, ic);
+        const int row = s_row[readlane(m_item, ic)];
+        const bool has_new = fused && i < nc && (keys - 1) / kBlock == lb;
+        const bool mine = has_new && (keys - 1) % TPI == tok0;
+        const size_t noff = ((size_t)row * a.num_kv_heads + kvh) * D * sizeof(T);
+        const buffer_rsrc_t rkn = make_rsrc(knew + noff, has_new ? D * (int)sizeof(T) : 0);
+        const buffer_rsrc_t rvn = make_rsrc(vnew + noff, has_new ? D * (int)sizeof(T) : 0);
+        const int o = mine ? 16 * chunk : D * (int)sizeof(T);
+        kn = buffer_load16(rkn, o);
+        vn = buffer_load16(rvn, o);
+      }
     };
 
     // A new piece at chunk block i: flush the open one, set up the new one, and
@@ -428,12 +471,24 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
     // is done once per score.  The weights go back through LDS as bf16, laid out so a
     // lane reads its token pairs as packed words and P.V is one dot2 per (head, dim,
     // token pair).  The denominator sums the same rounded weights.
-    auto compute_bf16 = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i, int u) {
+    auto compute_bf16 = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], const uint4 &kn,
+                            const uint4 &vn, int i, int u) {
       const int lb = readlane(m_lb, i);
       const bool bad = readlane(m_ok, i) == 0;
       const int keys = pc_keys;
       float *red = s_red[wave][u];
       uint32_t *pw = s_pw[wave][u];
+      if (fused && (keys - 1) / kBlock == lb) {
+        // The newest token (position keys-1) comes from k_new / v_new, not the pool.
+        const int jn = ((keys - 1) % kBlock) / TPI;
+        const bool mine = (keys - 1) % TPI == tok0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          if (j == jn && mine) {
+            kr[j] = kn;
+            vr[j] = vn;
+          }
+      }
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
@@ -601,20 +656,21 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
 
     // Ring of PF+1 register buffers: while block i is computed, blocks i+1..i+PF are
     // in flight, across piece boundaries.
-    uint4 kb[PF + 1][NV], vb[PF + 1][NV];
+    uint4 kb[PF + 1][NV], vb[PF + 1][NV], knb[PF + 1], vnb[PF + 1];
 #pragma unroll
-    for (int q = 0; q < PF; ++q) load(kb[q], vb[q], q);
+    for (int q = 0; q < PF; ++q) load(kb[q], vb[q], knb[q], vnb[q], q);
     for (int i0 = 0; i0 < nc; i0 += PF + 1) {
 #pragma unroll
       for (int u = 0; u <= PF; ++u) {
-        load(kb[(u + PF) % (PF + 1)], vb[(u + PF) % (PF + 1)], i0 + u + PF);
+        const int un = (u + PF) % (PF + 1);
+        load(kb[un], vb[un], knb[un], vnb[un], i0 + u + PF);
         const int i = i0 + u;
         if (i < nc) {
           if ((starts >> i) & 1ull) begin_piece(i);
           if constexpr (kF32)
             compute(kb[u], vb[u], i);
           else
-            compute_bf16(kb[u], vb[u], i, u);
+            compute_bf16(kb[u], vb[u], knb[u], vnb[u], i, u);
         }
       }
     }
@@ -648,16 +704,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   const int h = kvh * group + (g - kvh * p.num_head_groups) * HG + hh;
   const size_t base = (size_t)first * HG + hh;  // slot of piece i: base + i * HG
 
-  // pass 1: the largest lse over all pieces
-  float mx = lane < npieces ? p.ws_lse[base + (size_t)lane * HG] : -INFINITY;
-  for (int s0 = 64; s0 < npieces; s0 += 64)
-    if (s0 + lane < npieces) mx = fmaxf(mx, p.ws_lse[base + (size_t)(s0 + lane) * HG]);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor(mx, m));
-  // pass 2: weighted sum of the pieces' outputs, 8 pieces' loads in flight at a time
-  // (indices past the end are clamped to the last piece and weighted 0)
+  // One pass in batches of 8 pieces (indices past the end are clamped to the last
+  // piece and weighted 0): each batch's lse and o values are loaded together, and the
+  // running sums are rescaled when the running maximum rises.
   constexpr int kBatch = 8;
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
@@ -673,9 +724,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
 #pragma unroll
       for (int e = 0; e < DW; ++e) v[jj][e] = src[lane + 64 * e];
     }
+    float bm = M;
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj)
+      if (s0 + jj < npieces) bm = fmaxf(bm, lv[jj]);
+    if (bm == -INFINITY) continue;  // nothing with weight yet
+    const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - bm);
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < DW; ++e) o[e] *= r;
+    M = bm;
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
-      const float wj = (s0 + jj < npieces && lv[jj] != -INFINITY) ? fast_exp2(lv[jj] - mx) : 0.f;
+      const float wj = (s0 + jj < npieces && lv[jj] != -INFINITY) ? fast_exp2(lv[jj] - M) : 0.f;
       L += wj;
 #pragma unroll
       for (int e = 0; e < DW; ++e) o[e] = fmaf(wj, v[jj][e], o[e]);

@@ -51,6 +51,12 @@ struct AttnArgs {
   int num_q_heads, num_kv_heads, head_dim;
   int max_query_len;
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
+  // Fused slot write (all null otherwise): this step's new rows [total_q][Hkv][D] and
+  // their slots.  The decode kernel stores them into the pools and takes each decode
+  // row's newest key and value from k_new / v_new instead of the pool.
+  const void *k_new;
+  const void *v_new;
+  const int32_t *slot_mapping;
 };
 
 // Per-launch arguments of the decode and merge kernels.

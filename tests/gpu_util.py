@@ -58,6 +58,17 @@ class DeviceBatch:
         torch.cuda.synchronize()
         return out
 
+    def step_fused(self, out=None):
+        """The same step through paged_attention_varlen_with_write (one call)."""
+        b = self.b
+        out = pkv.attention_with_write(self.q, self.k_new, self.v_new, self.k_pool,
+                                       self.v_pool, self.slot_mapping, self.block_tables,
+                                       self.context_lens, self.query_start_loc,
+                                       scale=b.scale, max_context_len=b.max_context_len,
+                                       max_query_len=b.max_query_len, out=out)
+        torch.cuda.synchronize()
+        return out
+
 
 def out_f64(out: torch.Tensor) -> np.ndarray:
     return O.to_f64(to_raw(out), "bf16" if out.dtype == torch.bfloat16 else "f32")

@@ -137,6 +137,70 @@ def test_workload_full_size(name):
 
 
 # ---------------------------------------------------------------------------
+# the fused entry point (slot write + attention in one call)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_step_matches_oracle(name):
+    b = SMALL[name](3)
+    kp_ref, vp_ref, ref = O.step(b)
+    db = DeviceBatch(b)
+    out = db.step_fused()
+    assert to_raw(db.k_pool).tobytes() == kp_ref.tobytes(), "K pool after fused step"
+    assert to_raw(db.v_pool).tobytes() == vp_ref.tobytes(), "V pool after fused step"
+    _assert_close(b, out_f64(out), ref, name + " fused")
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_decode", "qwen3_1p7b_decode_640",
+                                  "shared_prefix_decode", "chunked_prefill_mixed"])
+def test_fused_full_size_equals_two_calls(name):
+    """Same bits as kv_write + attention (the newest key/value of each decode row is
+    taken from k_new / v_new instead of the pool, which holds the same values), and
+    the pools match the oracle's write."""
+    print(f"[case] fused workload {name}", flush=True)
+    b = make_config(name, 0)
+    o1 = to_raw(DeviceBatch(b).step())
+    db = DeviceBatch(b)
+    o2 = to_raw(db.step_fused())
+    kp_ref, vp_ref = O.kv_write(b.k_pool, b.v_pool, b.k_new, b.v_new, b.slot_mapping)
+    assert to_raw(db.k_pool).tobytes() == kp_ref.tobytes(), "K pool after fused step"
+    assert to_raw(db.v_pool).tobytes() == vp_ref.tobytes(), "V pool after fused step"
+    assert o1.tobytes() == o2.tobytes()
+
+
+def test_fused_newest_key_comes_from_k_new():
+    """The pool slot of each decode row's newest token holds NaN before the call (it is
+    written in the same launch), so a row that read that slot back would come out NaN.
+    One-hot probe through the fused call: every row puts weight exactly 1 on its newest
+    key and must return that token's new V row bit for bit."""
+    from workloads import bf16_round_bits
+    ctxs = [17, 32, 33, 250, 16]
+    b = _case("fused_probe", 7, dtype="bf16", num_q_heads=2, num_kv_heads=1, head_dim=128,
+              num_blocks=64, context_lens=ctxs, query_lens=[1] * len(ctxs), stale="nan")
+    d = b.head_dim
+    qf = np.zeros((b.total_q, 2, d), np.float32)
+    qf[:, :, 0] = 1.0
+    kpf = O.to_f64(b.k_pool, "bf16").astype(np.float32)
+    knf = np.zeros((b.total_q, 1, d), np.float32)
+    for s, c in enumerate(ctxs):
+        for j in range(c - 1):
+            kpf[int(b.block_tables[s][j // 16]), 0, j % 16, :] = 0.0
+            kpf[int(b.block_tables[s][j // 16]), 0, j % 16, 0] = j / 1024.0
+        knf[s, 0, 0] = (c - 1) / 1024.0
+    b.q, b.k_pool, b.k_new = bf16_round_bits(qf), bf16_round_bits(kpf), bf16_round_bits(knf)
+    nan = np.uint16(0x7FC0)
+    for t, slot in enumerate(b.slot_mapping):
+        b.k_pool[slot // 16, :, slot % 16, :] = nan
+        b.v_pool[slot // 16, :, slot % 16, :] = nan
+    b.scale = 1.0e6
+    out = out_f64(DeviceBatch(b).step_fused())
+    for s in range(len(ctxs)):
+        want = O.to_f64(b.v_new[s, 0], "bf16")
+        for h in range(2):
+            assert np.array_equal(out[s, h], want), f"seq {s} head {h}"
+
+
+# ---------------------------------------------------------------------------
 # invariants, GPU against GPU, bit for bit
 # ---------------------------------------------------------------------------
 
