@@ -2,7 +2,9 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the slot write of the step's new
-K/V (paged_kv_write) followed by varlen paged attention (paged_attention_varlen).
+K/V and varlen paged attention over the updated pools, issued as one
+paged_attention_varlen_with_write call (the same result as paged_kv_write followed by
+paged_attention_varlen; that two-call step is timed too and reported beside it).
 
 Default workload (the one the headline metric is quoted on): Llama-3.2-1B-shaped
 single-layer decode in bf16, 32 sequences, 32 query / 8 KV heads, head_dim 64,
@@ -16,9 +18,10 @@ Timing
   * W eager warm-up steps run first.  Then exactly K steps are captured into one HIP
     graph; after one untimed warm replay, the timed replay is bracketed by
     torch.cuda.synchronize() on both sides (one process, one GPU: no barrier needed).
-  * The attention call's average duration (`roofline.achieved`) is timed separately
-    with HIP events on the launch stream, in an eager loop queued behind a spin kernel
-    so the GPU runs the calls back to back.
+  * The step call's average duration (`roofline.achieved`) is timed separately with
+    HIP events on the launch stream, in an eager loop queued behind a spin kernel so
+    the GPU runs the calls back to back.  One call launches the decode kernel (which
+    also performs the slot write) and the split-K merge kernel; `roofline` covers both.
   * value = algorithmic bytes of one step / ms_per_step (GB/s).  Algorithmic bytes
     count every logical KV token of a sequence once (shared-prefix blocks once per
     physical block), plus q, out, table entries, lengths, and the write's new K/V
@@ -135,15 +138,28 @@ class Runner:
                            max_query_len=b.max_query_len, out=s.out,
                            workspace=self.ws[i % len(self.sets)])
 
+    def fused(self, i):
+        s = self.sets[i % len(self.sets)]
+        b = self.b
+        self.pkv.attention_with_write(s.q, s.k_new, s.v_new, s.k_pool, s.v_pool,
+                                      s.slot_mapping, s.block_tables, s.context_lens,
+                                      s.query_start_loc, scale=b.scale,
+                                      max_context_len=b.max_context_len,
+                                      max_query_len=b.max_query_len, out=s.out,
+                                      workspace=self.ws[i % len(self.sets)])
+
     def step(self, i):
+        self.fused(i)
+
+    def step_two_calls(self, i):
         self.write(i)
         self.attend(i)
 
 
-def time_graph(r: Runner, steps: int, warmup: int, write=True) -> float:
-    """ms per step from one HIP graph of exactly `steps` steps."""
+def time_graph(r: Runner, steps: int, warmup: int, fn=None) -> float:
+    """ms per step from one HIP graph of exactly `steps` calls of fn (default r.step)."""
     torch = r.torch
-    fn = r.step if write else r.attend
+    fn = fn or r.step
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -163,22 +179,22 @@ def time_graph(r: Runner, steps: int, warmup: int, write=True) -> float:
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def time_calls(r: Runner, calls: int, write_between=True) -> float:
-    """Average duration (ms) of the attention call, from HIP events on its stream."""
+def time_calls(r: Runner, calls: int, fn=None) -> float:
+    """Average duration (ms) of one call of fn (default r.step), from HIP events
+    recorded on the stream the kernels are launched on."""
     torch = r.torch
+    fn = fn or r.step
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(calls)]
     for i in range(2):
-        r.step(i)
+        fn(i)
     torch.cuda.synchronize()
     # queue everything behind a spin kernel so the calls run back to back on the GPU
     torch.cuda._sleep(int(2e8))
     for i in range(calls):
-        if write_between:
-            r.write(i)
         evs[i][0].record(stream)
-        r.attend(i)
+        fn(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / calls
@@ -241,6 +257,97 @@ def traffic_for(workload: str):
     return None if ent is None else ent.get("bytes_per_call")
 
 
+def write_traffic(out_dir: str, workload: str = MAIN) -> dict:
+    """Build profiles/traffic.json from rocprofv3 --pmc runs of this script: FETCH_SIZE
+    and WRITE_SIZE of `bench.py --only-main` (one pass each) and of
+    `bench.py --copy-calibration` (5 plain 256 MiB copies), in `out_dir`/pmc_bench_<C>
+    and `out_dir`/pmc_copy_<C>.  Counts are KiB per dispatch; each counter is scaled
+    by copy bytes / what it reads for the copies.  bytes_per_call covers the kernels
+    of one step call (all kernels of this library)."""
+    import collections
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                acc[row["Kernel_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        return acc
+
+    res = {"workloads": {}}
+    copy_bytes = 256 << 20
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per_kernel(os.path.join(out_dir, f"pmc_copy_{c}"), c)
+        vals = [v for k, ds in cp.items() if "copy" in k.lower() or "elementwise" in k
+                for v in ds.values() if v > 100000]
+        kib = sorted(vals)[len(vals) // 2]
+        scale[c] = copy_bytes / (kib * 1024.0)
+        res.setdefault("calibration", {})[c.lower() + "_kib"] = kib
+    res["calibration"]["copy_bytes"] = copy_bytes
+    res["calibration"]["fetch_scale"] = round(scale["FETCH_SIZE"], 4)
+    res["calibration"]["write_scale"] = round(scale["WRITE_SIZE"], 4)
+    kernels = {}
+    total = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        pk = per_kernel(os.path.join(out_dir, f"pmc_bench_{c}"), c)
+        tot = 0.0
+        for k, ds in pk.items():
+            if "pkv::" not in k:
+                continue
+            short = k.split("<")[0].replace("void ", "").replace("pkv::", "")
+            med = sorted(ds.values())[len(ds) // 2]
+            kernels.setdefault(short, {})[c] = med
+            kernels[short]["dispatches"] = len(ds)
+            tot += med
+        total[c] = tot * 1024.0 * scale[c]
+    from workloads import make_config
+    b = make_config(workload, 0)
+    res["workloads"][workload] = {
+        "bytes_per_call": int(total["FETCH_SIZE"] + total["WRITE_SIZE"]),
+        "fetch_bytes": int(total["FETCH_SIZE"]), "write_bytes": int(total["WRITE_SIZE"]),
+        "algorithmic_bytes": attention_bytes(b) + write_bytes(b),
+        "per_kernel_kib_raw": kernels}
+    res["about"] = ("HBM traffic per step call of the headline workload, from rocprofv3 "
+                    "FETCH_SIZE/WRITE_SIZE scaled by a 256 MiB copy calibration; valid "
+                    "only while the kernel sources hash to source_sha256")
+    res["source_sha256"] = kernel_source_hash()
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def measure_chunk(bx, calls: int) -> dict:
+    """The 2,017-row prefill chunk of the mixed step alone (sequence 0 only): the
+    attention call launches prefill_mfma_kernel only; HIP events per call."""
+    import copy
+
+    import torch
+
+    bc = copy.copy(bx)
+    bc.block_tables = bx.block_tables[:1]
+    bc.context_lens = bx.context_lens[:1]
+    q0 = int(bx.query_start_loc[1])
+    bc.query_start_loc = bx.query_start_loc[:2]
+    bc.q, bc.k_new, bc.v_new = bx.q[:q0], bx.k_new[:q0], bx.v_new[:q0]
+    bc.slot_mapping = bx.slot_mapping[:q0]
+    rc = Runner(bc, 4)
+    rc.write(0)
+    cms = time_calls(rc, calls, fn=rc.attend)
+    cfl = chunk_flops(bc)
+    tfs = cfl / (cms * 1e-3) / 1e12
+    del rc
+    torch.cuda.empty_cache()
+    return {"workload": "chunked_prefill_mixed: the 2,017-row chunk alone",
+            "bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_MFMA_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4), "flops": cfl,
+            "avg_ms": round(cms, 5), "kernel": "prefill_mfma_kernel"}
+
+
 # ---------------------------------------------------------------------------
 
 def main() -> int:
@@ -254,7 +361,15 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--only-chunk", action="store_true",
+                    help="only time the prefill chunk of the mixed step (profiling)")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="(host only) summarise rocprofv3 --pmc runs found in DIR into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.write_traffic), indent=1))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
@@ -280,6 +395,11 @@ def main() -> int:
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    if args.only_chunk:
+        print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
+                                                                     0), args.steps)}))
+        return 0
+
     # ---- the headline workload ----
     log(f"generating {MAIN}")
     b = make_config(MAIN, 0)
@@ -287,15 +407,17 @@ def main() -> int:
     r = Runner(b, rot)
     log(f"timing {args.steps} graph-captured steps over {rot} rotating copies")
     ms = time_graph(r, args.steps, args.warmup)
-    attn_ms = time_calls(r, args.steps)
+    ms_two = time_graph(r, args.steps, args.warmup, fn=r.step_two_calls)
+    call_ms = time_calls(r, args.steps)
     abytes, wbytes = attention_bytes(b), write_bytes(b)
     value = (abytes + wbytes) / (ms * 1e-3) / 1e9
-    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    achieved = (abytes + wbytes) / (call_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_for(MAIN),
-            "kernel": "paged_attention_varlen (decode_streamk_kernel + merge_kernel)",
-            "algorithmic_bytes": abytes, "avg_ms": round(attn_ms, 5)}
+            "kernel": "paged_attention_varlen_with_write: decode_streamk_kernel (with "
+                      "the slot write) + merge_kernel, one call",
+            "algorithmic_bytes": abytes + wbytes, "avg_ms": round(call_ms, 5)}
     del r
     torch.cuda.empty_cache()
 
@@ -309,6 +431,9 @@ def main() -> int:
                    "pool_blocks": 8192, "seed": 0, "rotating_copies": rot,
                    "timed_region": "HIP graph of the K steps"},
         "roofline": roof,
+        "two_call_step": {"ms_per_step": round(ms_two, 5),
+                          "GBs": round((abytes + wbytes) / (ms_two * 1e-3) / 1e9, 1),
+                          "calls": "paged_kv_write then paged_attention_varlen"},
     }
 
     # ---- the other workloads (context lines, same protocol) ----
@@ -322,39 +447,19 @@ def main() -> int:
             msx = time_graph(rx, args.steps, args.warmup)
             ax = time_calls(rx, args.steps)
             ab, wb = attention_bytes(bx), write_bytes(bx)
-            ent = {"ms_per_step": round(msx, 5), "attn_ms": round(ax, 5),
+            ent = {"ms_per_step": round(msx, 5), "call_ms": round(ax, 5),
                    "step_GBs": round((ab + wb) / (msx * 1e-3) / 1e9, 1),
-                   "attn_GBs": round(ab / (ax * 1e-3) / 1e9, 1),
-                   "attn_hbm_frac": round(ab / (ax * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "call_GBs": round((ab + wb) / (ax * 1e-3) / 1e9, 1),
+                   "call_hbm_frac": round((ab + wb) / (ax * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             if name == "shared_prefix_decode":
                 lb = attention_bytes(bx, unique=False)
-                ent["attn_logical_GBs"] = round(lb / (ax * 1e-3) / 1e9, 1)
+                ent["call_logical_GBs"] = round((lb + wb) / (ax * 1e-3) / 1e9, 1)
             if name == "chunked_prefill_mixed":
                 fl = chunk_flops(bx)
                 ent["step_TFLOPs"] = round(fl / (msx * 1e-3) / 1e12, 2)
                 del rx
                 torch.cuda.empty_cache()
-                # the chunk alone: sequence 0 only
-                from workloads.synth import PagedBatch  # noqa: F401
-                import copy
-                bc = copy.copy(bx)
-                bc.block_tables = bx.block_tables[:1]
-                bc.context_lens = bx.context_lens[:1]
-                q0 = int(bx.query_start_loc[1])
-                bc.query_start_loc = bx.query_start_loc[:2]
-                bc.q, bc.k_new, bc.v_new = bx.q[:q0], bx.k_new[:q0], bx.v_new[:q0]
-                bc.slot_mapping = bx.slot_mapping[:q0]
-                rc = Runner(bc, 4)
-                cms = time_calls(rc, args.steps, write_between=False)
-                cfl = chunk_flops(bc)
-                tfs = cfl / (cms * 1e-3) / 1e12
-                result["prefill_chunk"] = {
-                    "workload": "chunked_prefill_mixed: the 2,017-row chunk alone",
-                    "bound": "mfma", "achieved": round(tfs, 2),
-                    "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                    "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4), "flops": cfl,
-                    "avg_ms": round(cms, 5), "kernel": "prefill_mfma_kernel"}
-                del rc
+                result["prefill_chunk"] = measure_chunk(bx, args.steps)
             else:
                 del rx
             torch.cuda.empty_cache()
