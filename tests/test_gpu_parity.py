@@ -200,6 +200,72 @@ def test_fused_newest_key_comes_from_k_new():
             assert np.array_equal(out[s, h], want), f"seq {s} head {h}"
 
 
+def test_workspace_reused_across_batches():
+    """One workspace serves consecutive calls on different batches: every call must
+    merge only its own split-K partial results (a stale partial or descriptor from the
+    previous call would corrupt the next one)."""
+    import paged_kv_cache_290_amd as pkv
+    batches = [make_config("llama32_1b_decode", s) for s in (3, 4)]
+    need = max(pkv.workspace_size(b.num_seqs, b.total_q, b.num_q_heads, b.num_kv_heads,
+                                  b.head_dim, b.max_context_len, torch.bfloat16)
+               for b in batches)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dbs = [DeviceBatch(b) for b in batches]
+    for db in dbs:
+        db.write()
+    for k in (0, 1, 0, 1):
+        b, db = batches[k], dbs[k]
+        out = pkv.attention(db.q, db.k_pool, db.v_pool, db.block_tables, db.context_lens,
+                            db.query_start_loc, scale=b.scale,
+                            max_context_len=b.max_context_len, max_query_len=1,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        kp, vp = to_raw(db.k_pool), to_raw(db.v_pool)
+        rows = list(range(0, b.total_q, 3))
+        _assert_close(b, out_f64(out)[rows], oracle_rows(b, kp, vp, rows), f"call on batch {k}")
+
+
+def test_graph_replays_match_eager():
+    """Two fused steps (different batches, one shared workspace) captured in one HIP
+    graph and replayed three times, with eager work and synchronisations between the
+    replays; every replay must equal the eager results bit for bit."""
+    import paged_kv_cache_290_amd as pkv
+    batches = [make_config("qwen3_1p7b_decode_640", s) for s in (5, 6)]
+    need = max(pkv.workspace_size(b.num_seqs, b.total_q, b.num_q_heads, b.num_kv_heads,
+                                  b.head_dim, b.max_context_len, torch.bfloat16)
+               for b in batches)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dbs = [DeviceBatch(b) for b in batches]
+    outs = [torch.empty_like(db.q) for db in dbs]
+
+    def step_all():
+        for b, db, o in zip(batches, dbs, outs):
+            pkv.attention_with_write(db.q, db.k_new, db.v_new, db.k_pool, db.v_pool,
+                                     db.slot_mapping, db.block_tables, db.context_lens,
+                                     db.query_start_loc, scale=b.scale,
+                                     max_context_len=b.max_context_len, max_query_len=1,
+                                     out=o, workspace=ws)
+
+    step_all()
+    torch.cuda.synchronize()
+    eager = [to_raw(o).copy() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step_all()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, o in enumerate(outs):
+            assert to_raw(o).tobytes() == eager[k].tobytes(), f"replay {rep} batch {k}"
+
+
 # ---------------------------------------------------------------------------
 # invariants, GPU against GPU, bit for bit
 # ---------------------------------------------------------------------------
