@@ -13,8 +13,10 @@
  *     Chunked Prefill subsection: a long prompt runs as consecutive slices mixed with
  *     other requests' single decode tokens in one step.
  *
- * The library is stateless.  The caller (a scheduler) owns every buffer.  The library
- * never allocates, frees or synchronises; calls are asynchronous on `stream`.
+ * The GPU entry points are stateless.  The caller (a scheduler) owns every buffer; they
+ * never allocate, free or synchronise, and run asynchronously on `stream`.  The block
+ * allocator at the end of this header is a host object the caller creates and
+ * destroys (it holds only host memory).
  *
  * Common conventions
  *   - All array pointers are DEVICE pointers on the current HIP device, C-contiguous.
@@ -48,7 +50,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes   */
   PKV_ERR_UNSUPPORTED = 2, /* block_size != 16, head_dim not 64/128, bad dtype   */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required         */
-  PKV_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch        */
+  PKV_ERR_LAUNCH = 4,      /* the HIP runtime reported an error at launch        */
+  PKV_ERR_OUT_OF_BLOCKS = 5 /* the block allocator has too few free blocks       */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -149,6 +152,74 @@ pkv_status paged_attention_varlen_with_write(
     int32_t max_context_len, int32_t max_query_len, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
     pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block bookkeeping (serving-engine KV page, section 2: "blocks and block table" -- a
+ * request takes a new 16-token block when its current one fills; "block sharing" --
+ * requests sharing a prompt name the same blocks, each block has a reference count,
+ * and a shared block is copied only when a holder appends into it).
+ *
+ * pkv_block_allocator is a host object over physical blocks 0..num_blocks-1 of one
+ * pool pair.  Tables passed to it are HOST int32 arrays (a request's logical->physical
+ * block list, the row that goes into block_tables).  Not thread-safe.  The lowest
+ * free block is always taken first.  Every call either succeeds or changes nothing.
+ */
+typedef struct pkv_block_allocator pkv_block_allocator;
+
+/* Create an allocator with every block free.  *out receives the handle. */
+pkv_status pkv_allocator_create(int32_t num_blocks, pkv_block_allocator **out);
+void pkv_allocator_destroy(pkv_block_allocator *alloc);
+/* Free blocks (-1 for a NULL handle); reference count of a block (-1 if out of range). */
+int32_t pkv_allocator_num_free(const pkv_block_allocator *alloc);
+int32_t pkv_allocator_refcount(const pkv_block_allocator *alloc, int32_t block);
+
+/*
+ * pkv_allocator_fork -- another request now shares the num_used blocks of `table`
+ * (one more reference each; the caller copies the table row for the new request).
+ * INVALID_ARG if an entry is not a held block.
+ */
+pkv_status pkv_allocator_fork(pkv_block_allocator *alloc, const int32_t *table,
+                              int32_t num_used);
+
+/*
+ * pkv_allocator_release -- a request is done with the num_used blocks of `table`: one
+ * reference fewer each; a block with none left is free again.
+ */
+pkv_status pkv_allocator_release(pkv_block_allocator *alloc, const int32_t *table,
+                                 int32_t num_used);
+
+/*
+ * pkv_allocator_append -- make room for num_new tokens after context_len cached ones
+ * of the request whose table is `table` (ceil(context_len/16) used entries, room for
+ * max_blocks_per_seq; updated in place).  Writes the flat pool slot of every new
+ * token to slots[num_new] (the slot_mapping for paged_kv_write).  If the request's
+ * partly filled last block is shared, the request first moves to a private copy:
+ * the (source, destination) pair is written to copies[0..1], *num_copies = 1, and
+ * the caller must run paged_kv_copy_blocks on it before writing the new tokens.
+ * Errors: OUT_OF_BLOCKS if the pool cannot hold the append; INVALID_ARG for bad
+ * arguments, a table entry that is not a held block, more blocks than
+ * max_blocks_per_seq, or max_copies == 0 when a copy is needed.
+ */
+pkv_status pkv_allocator_append(pkv_block_allocator *alloc, int32_t *table,
+                                int32_t max_blocks_per_seq, int32_t context_len,
+                                int32_t num_new, int32_t *slots, int32_t *copies,
+                                int32_t max_copies, int32_t *num_copies);
+
+/*
+ * paged_kv_copy_blocks -- copy-on-write copies on the GPU: for each pair i, every row
+ * (all kv heads and offsets) of physical block copies[2i] is copied bit for bit to
+ * block copies[2i+1], in both pools.
+ *
+ *   k_pool, v_pool  [num_blocks][num_kv_heads][16][head_dim]    (device, written)
+ *   copies          int32 [num_copies][2] (source, destination) (device)
+ * Pairs with an id outside [0, num_blocks) are skipped.  Destinations must be
+ * distinct and not also sources in the same call (as the allocator produces them).
+ * num_copies == 0 is a no-op.  Asynchronous on `stream`.
+ */
+pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copies,
+                                int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                                void *stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *pkv_status_string(pkv_status status);

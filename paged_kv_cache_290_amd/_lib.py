@@ -15,6 +15,7 @@ PKV_ERR_INVALID_ARG = 1
 PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE = 3
 PKV_ERR_LAUNCH = 4
+PKV_ERR_OUT_OF_BLOCKS = 5
 PKV_F32 = 0
 PKV_BF16 = 1
 
@@ -32,6 +33,16 @@ SIGNATURES = {
                                                          _i32, _i32, _i32, _i32, _i32,
                                                          _i32, _i32, _f32, ctypes.c_int,
                                                          _vp, _sz, _vp]),
+    "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
+    "pkv_allocator_destroy": (None, [_vp]),
+    "pkv_allocator_num_free": (_i32, [_vp]),
+    "pkv_allocator_refcount": (_i32, [_vp, _i32]),
+    "pkv_allocator_fork": (ctypes.c_int, [_vp, _vp, _i32]),
+    "pkv_allocator_release": (ctypes.c_int, [_vp, _vp, _i32]),
+    "pkv_allocator_append": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
+                                            ctypes.POINTER(_i32)]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            ctypes.c_int, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),

@@ -87,6 +87,7 @@ const char *pkv_status_string(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
   }
   return "unknown status";
 }

@@ -1,0 +1,217 @@
+// Block bookkeeping around the paged KV pool: a host-side reference-counted block
+// allocator with copy-on-write appends, and the HIP kernel that performs the block
+// copies on the caller's stream.
+//
+// Method (pages cited by title and section):
+//  * Serving-engine KV page (ttlab), section 2 "PagedAttention", "blocks and block
+//    table": 16-token blocks may sit anywhere in free memory, and a request takes one
+//    new block when its current block fills, i.e. when the token at a position that is
+//    a multiple of 16 is appended.
+//  * Same page, "block sharing": requests sharing a prompt (parallel sampling, beam
+//    search) name the same blocks; each block has a reference count, and a block is
+//    copied only when one of its holders must append into it (copy-on-write).
+//
+// Policy choices the pages leave open: the lowest-numbered free block is taken first;
+// an append that does not fit changes nothing; a copy moves whole blocks (every kv
+// head and offset) in both pools.
+#include <stdint.h>
+
+#include <functional>
+#include <new>
+#include <queue>
+#include <vector>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+// ---------------------------------------------------------------------------
+// host allocator
+// ---------------------------------------------------------------------------
+
+struct pkv_block_allocator {
+  std::vector<int32_t> ref;  // reference count per physical block (0 = free)
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_ids;
+};
+
+namespace {
+
+bool valid_held(const pkv_block_allocator *a, int32_t b) {
+  return b >= 0 && b < (int32_t)a->ref.size() && a->ref[b] > 0;
+}
+
+int32_t take(pkv_block_allocator *a) {
+  const int32_t b = a->free_ids.top();
+  a->free_ids.pop();
+  a->ref[b] = 1;
+  return b;
+}
+
+void drop(pkv_block_allocator *a, int32_t b) {
+  if (--a->ref[b] == 0) a->free_ids.push(b);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// block copy kernel: each thread moves 16-byte pieces of (pair, pool) regions
+// ---------------------------------------------------------------------------
+
+namespace pkv {
+
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    uint4 *__restrict__ k_pool, uint4 *__restrict__ v_pool, const int32_t *__restrict__ pairs,
+    int num_pairs, int num_blocks, int64_t block_vecs) {
+  const int64_t total = (int64_t)num_pairs * 2 * block_vecs;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t per_pair = 2 * block_vecs;
+    const int pair = (int)(idx / per_pair);
+    const int64_t rem = idx - (int64_t)pair * per_pair;
+    const bool is_v = rem >= block_vecs;
+    const int64_t piece = is_v ? rem - block_vecs : rem;
+    const int src = pairs[2 * pair];
+    const int dst = pairs[2 * pair + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
+    uint4 *pool = is_v ? v_pool : k_pool;
+    pool[(int64_t)dst * block_vecs + piece] = pool[(int64_t)src * block_vecs + piece];
+  }
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+pkv_status pkv_allocator_create(int32_t num_blocks, pkv_block_allocator **out) {
+  if (!out || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  *out = nullptr;
+  pkv_block_allocator *a = new (std::nothrow) pkv_block_allocator();
+  if (!a) return PKV_ERR_OUT_OF_BLOCKS;
+  try {
+    a->ref.assign(num_blocks, 0);
+    std::vector<int32_t> ids(num_blocks);
+    for (int32_t i = 0; i < num_blocks; ++i) ids[i] = i;
+    a->free_ids = decltype(a->free_ids)(std::greater<int32_t>(), std::move(ids));
+  } catch (...) {
+    delete a;
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  *out = a;
+  return PKV_OK;
+}
+
+void pkv_allocator_destroy(pkv_block_allocator *alloc) { delete alloc; }
+
+int32_t pkv_allocator_num_free(const pkv_block_allocator *alloc) {
+  return alloc ? (int32_t)alloc->free_ids.size() : -1;
+}
+
+int32_t pkv_allocator_refcount(const pkv_block_allocator *alloc, int32_t block) {
+  if (!alloc || block < 0 || block >= (int32_t)alloc->ref.size()) return -1;
+  return alloc->ref[block];
+}
+
+pkv_status pkv_allocator_fork(pkv_block_allocator *alloc, const int32_t *table,
+                              int32_t num_used) {
+  if (!alloc || num_used < 0 || (num_used > 0 && !table)) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < num_used; ++i)
+    if (!valid_held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < num_used; ++i) ++alloc->ref[table[i]];
+  return PKV_OK;
+}
+
+pkv_status pkv_allocator_release(pkv_block_allocator *alloc, const int32_t *table,
+                                 int32_t num_used) {
+  if (!alloc || num_used < 0 || (num_used > 0 && !table)) return PKV_ERR_INVALID_ARG;
+  // A table naming one block twice would drop it twice: count first, then check.
+  std::vector<int32_t> uses;
+  for (int32_t i = 0; i < num_used; ++i) {
+    if (!valid_held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
+  }
+  try {
+    uses.assign(alloc->ref.size(), 0);
+  } catch (...) {
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  for (int32_t i = 0; i < num_used; ++i)
+    if (++uses[table[i]] > alloc->ref[table[i]]) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < num_used; ++i) drop(alloc, table[i]);
+  return PKV_OK;
+}
+
+pkv_status pkv_allocator_append(pkv_block_allocator *alloc, int32_t *table,
+                                int32_t max_blocks_per_seq, int32_t context_len,
+                                int32_t num_new, int32_t *slots, int32_t *copies,
+                                int32_t max_copies, int32_t *num_copies) {
+  if (num_copies) *num_copies = 0;
+  if (!alloc || context_len < 0 || num_new < 0 || max_blocks_per_seq < 0 ||
+      max_copies < 0 || !num_copies || (num_new > 0 && (!table || !slots)))
+    return PKV_ERR_INVALID_ARG;
+  if (num_new == 0) return PKV_OK;
+  const int64_t end = (int64_t)context_len + num_new;
+  if ((end + kBlock - 1) / kBlock > max_blocks_per_seq) return PKV_ERR_INVALID_ARG;
+  const int32_t used = (context_len + kBlock - 1) / kBlock;
+  for (int32_t lb = 0; lb < used; ++lb)
+    if (!valid_held(alloc, table[lb])) return PKV_ERR_INVALID_ARG;
+  // What the append needs, before anything changes: a block per 16-token boundary
+  // crossed, and a copy of the partly filled last block if it is shared.
+  int64_t need = 0;
+  int32_t ncopy = 0;
+  for (int64_t pos = context_len; pos < end; ++pos)
+    if (pos % kBlock == 0) ++need;
+  if (context_len % kBlock != 0 && alloc->ref[table[used - 1]] > 1) {
+    ++need;
+    ++ncopy;
+  }
+  if (ncopy > max_copies || (ncopy > 0 && !copies)) return PKV_ERR_INVALID_ARG;
+  if (need > (int64_t)alloc->free_ids.size()) return PKV_ERR_OUT_OF_BLOCKS;
+
+  if (ncopy) {
+    const int32_t src = table[used - 1];
+    const int32_t dst = take(alloc);
+    --alloc->ref[src];  // still held by the other requests
+    table[used - 1] = dst;
+    copies[0] = src;
+    copies[1] = dst;
+  }
+  for (int64_t pos = context_len; pos < end; ++pos) {
+    const int32_t lb = (int32_t)(pos / kBlock);
+    const int32_t off = (int32_t)(pos % kBlock);
+    if (off == 0) table[lb] = take(alloc);
+    slots[pos - context_len] = table[lb] * kBlock + off;
+  }
+  *num_copies = ncopy;
+  return PKV_OK;
+}
+
+pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copies,
+                                int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                                void *stream) {
+  if ((dtype != PKV_F32 && dtype != PKV_BF16) || block_size != kBlock ||
+      (head_dim != 64 && head_dim != 128))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_copies < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (num_copies == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !copies) return PKV_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)num_kv_heads * kBlock * head_dim *
+                              (dtype == PKV_F32 ? 4 : 2);
+  const int64_t block_vecs = block_bytes / 16;
+  const int64_t total = (int64_t)num_copies * 2 * block_vecs;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  const int64_t want = (total + kThreads - 1) / kThreads;
+  const int grid = (int)(want < (int64_t)cus * 8 ? want : (int64_t)cus * 8);
+  copy_blocks_kernel<<<dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint4 *>(k_pool), static_cast<uint4 *>(v_pool), copies, num_copies,
+      num_blocks, block_vecs);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -193,3 +193,90 @@ def validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
         ptr(bt), ptr(cl), ptr(qsl), ptr(sm), cl.shape[0], int(qsl[-1]) if qsl.size else 0,
         num_blocks, bt.shape[1] if bt.ndim == 2 else 0, ctypes.byref(bad))
     return st == _lib.PKV_OK, bad.value
+
+
+class BlockAllocator:
+    """Host reference-counted allocator of physical blocks (pkv_allocator_* in the C
+    ABI).  Tables are Python lists of block ids (a request's block_tables row)."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = _lib.load()
+        h = ctypes.c_void_p()
+        _lib.check("pkv_allocator_create", self._lib.pkv_allocator_create(num_blocks,
+                                                                          ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+    def num_free(self) -> int:
+        return int(self._lib.pkv_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_allocator_refcount(self._h, block))
+
+    @staticmethod
+    def _arr(table, extra: int = 0):
+        import numpy as np
+
+        a = np.zeros(len(table) + extra, dtype=np.int32)
+        a[:len(table)] = table
+        return a
+
+    def fork(self, table) -> list:
+        a = self._arr(table)
+        _lib.check("pkv_allocator_fork",
+                   self._lib.pkv_allocator_fork(self._h, a.ctypes.data, len(table)))
+        return list(table)
+
+    def release(self, table) -> None:
+        a = self._arr(table)
+        _lib.check("pkv_allocator_release",
+                   self._lib.pkv_allocator_release(self._h, a.ctypes.data, len(table)))
+
+    def append(self, table: list, context_len: int, num_new: int, max_blocks: int = 1 << 20):
+        """Room for num_new tokens after context_len; `table` (list) is updated in
+        place.  Returns (slots, copies) like the C call: slots of the new tokens and
+        the (source, destination) pairs to copy first."""
+        import numpy as np
+
+        used = (context_len + 15) // 16
+        end_blocks = (context_len + num_new + 15) // 16
+        arr = self._arr(table[:used], max(end_blocks - used, 0))
+        slots = np.zeros(max(num_new, 1), dtype=np.int32)
+        copies = np.zeros(2, dtype=np.int32)
+        ncopy = ctypes.c_int32(0)
+        st = self._lib.pkv_allocator_append(self._h, arr.ctypes.data,
+                                            min(max_blocks, len(arr)), context_len,
+                                            num_new, slots.ctypes.data, copies.ctypes.data,
+                                            1, ctypes.byref(ncopy))
+        _lib.check("pkv_allocator_append", st)
+        table[:] = [int(x) for x in arr[:end_blocks]]
+        pairs = [(int(copies[0]), int(copies[1]))] if ncopy.value else []
+        return [int(x) for x in slots[:num_new]], pairs
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, copies: torch.Tensor,
+                stream=None) -> None:
+    """Copy whole blocks in both pools: copies is an int32 [n, 2] (source, destination)
+    device tensor (paged_kv_copy_blocks)."""
+    dev = k_pool.device
+    for n, t in (("k_pool", k_pool), ("v_pool", v_pool), ("copies", copies)):
+        _on_gpu(n, t, dev)
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    _require(copies.dtype == torch.int32 and copies.dim() == 2 and copies.shape[1] == 2,
+             "copies must be int32 [n, 2]")
+    nb, hkv, bs, d = k_pool.shape
+    st = _lib.load().paged_kv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(),
+                                          copies.data_ptr(), copies.shape[0], nb, hkv, d,
+                                          bs, _dtype_code(k_pool), _stream_handle(stream))
+    _lib.check("paged_kv_copy_blocks", st)
