@@ -348,6 +348,50 @@ def measure_chunk(bx, calls: int) -> dict:
             "avg_ms": round(cms, 5), "kernel": "prefill_mfma_kernel"}
 
 
+def measure_block_copy(calls: int, pairs: int = 1024) -> dict:
+    """Copy-on-write block copies (paged_kv_copy_blocks) on a Qwen3-1.7B-shaped pool
+    (8 kv heads, d=128, bf16: 32 KiB per block and pool): `pairs` random (source,
+    destination) pairs per call, both pools.  Algorithmic bytes per call = every
+    copied byte read once and written once.  Four pools are rotated (over 1 GiB in
+    total) so the copies come from HBM."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_290_amd as pkv
+
+    hkv, d, nb = 8, 128, 4 * pairs
+    rng = np.random.Generator(np.random.PCG64(0))
+    sets = []
+    for _ in range(4):
+        k = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda").normal_()
+        v = torch.empty_like(k).normal_()
+        perm = rng.permutation(nb)[:2 * pairs].reshape(pairs, 2)
+        sets.append((k, v, torch.from_numpy(perm.astype(np.int32)).cuda()))
+    stream = torch.cuda.current_stream()
+    for k, v, c in sets:
+        pkv.copy_blocks(k, v, c)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    torch.cuda._sleep(int(2e8))
+    for i in range(calls):
+        k, v, c = sets[i % 4]
+        evs[i][0].record(stream)
+        pkv.copy_blocks(k, v, c)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / calls
+    nbytes = pairs * 2 * (hkv * 16 * d * 2) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": f"{pairs} copy-on-write block copies, 8 kv heads x 16 x 128 bf16 "
+                        "blocks, both pools", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "avg_ms": round(ms, 5),
+            "kernel": "copy_blocks_kernel"}
+
+
 # ---------------------------------------------------------------------------
 
 def main() -> int:
@@ -363,6 +407,8 @@ def main() -> int:
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
     ap.add_argument("--only-chunk", action="store_true",
                     help="only time the prefill chunk of the mixed step (profiling)")
+    ap.add_argument("--only-copy", action="store_true",
+                    help="only time the copy-on-write block copies (profiling)")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="(host only) summarise rocprofv3 --pmc runs found in DIR into "
                          "profiles/traffic.json and exit")
@@ -395,6 +441,9 @@ def main() -> int:
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    if args.only_copy:
+        print(json.dumps({"block_copy": measure_block_copy(args.steps)}))
+        return 0
     if args.only_chunk:
         print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
                                                                      0), args.steps)}))
@@ -465,6 +514,8 @@ def main() -> int:
             torch.cuda.empty_cache()
             extra[name] = ent
         result["workloads"] = extra
+        log("timing copy-on-write block copies")
+        result["block_copy"] = measure_block_copy(args.steps)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
