@@ -392,6 +392,133 @@ def measure_block_copy(calls: int, pairs: int = 1024) -> dict:
             "kernel": "copy_blocks_kernel"}
 
 
+
+def measure_planned_prefill(reps: int = 3) -> dict:
+    """Chunked prefill driven by the library's planner: an 8,192-token prompt arrives
+    while 31 requests decode (contexts U[300, 4096], Qwen3-1.7B heads 16q/8kv, d=128,
+    bf16) under a 2,048-token step budget.  Each step is planned on the host
+    (pkv_plan_step, pkv_build_step through the binding), its metadata goes to the
+    device in one pinned host-to-device copy, the fused write + attention call runs,
+    and the host waits for the step (the next step's plan needs its result).  Reports
+    the host planning time per step, the GPU time per step (HIP events around the
+    step's calls), and the wall time of the whole prefill with its tokens/s.  The
+    per-step q, k_new and v_new come from buffers filled before timing."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_290_amd as pkv
+
+    hq, hkv, d, nb, budget, plen = 16, 8, 128, 8192, 2048, 8192
+    rng = np.random.Generator(np.random.PCG64(0))
+    dec_ctx = [int(c) for c in rng.integers(300, 4096, size=31, endpoint=True)]
+    max_blocks = plen // 16 + 1
+    nreq = len(dec_ctx) + 1
+
+    def fresh():
+        alloc = pkv.BlockAllocator(nb)
+        tables = np.full((nreq, max_blocks), -1, dtype=np.int32)
+        for r, c in enumerate(dec_ctx):
+            t = []
+            alloc.append(t, 0, c - 1)
+            tables[r, :len(t)] = t
+        prompt = np.array([c - 1 for c in dec_ctx] + [plen], dtype=np.int32)
+        done = prompt.copy()
+        done[-1] = 0
+        return alloc, tables, prompt, done
+
+    def advance(done, q):
+        done += np.asarray(q, dtype=np.int32)
+
+    # host planning alone
+    plan_s, nplan = 0.0, 0
+    for _ in range(20):
+        alloc, tables, prompt, done = fresh()
+        while done[-1] < prompt[-1]:
+            t0 = time.perf_counter()
+            q = pkv.plan_step(prompt, done, budget)
+            alloc.build_step(tables, done, q, max_blocks)
+            plan_s += time.perf_counter() - t0
+            nplan += 1
+            advance(done, q)
+        alloc.close()
+
+    kp = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    qb = torch.empty((budget, hq, d), dtype=torch.bfloat16, device="cuda").normal_()
+    knb = torch.empty((budget, hkv, d), dtype=torch.bfloat16, device="cuda").normal_()
+    vnb = torch.empty_like(knb).normal_()
+    out = torch.empty_like(qb)
+    ws = torch.empty(pkv.workspace_size(nreq, budget, hq, hkv, d, plen + 1, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    o_bt, o_ctx = 0, nreq * max_blocks
+    o_qsl, o_sl = o_ctx + nreq, o_ctx + 2 * nreq + 1
+    o_cp, total_i32 = o_sl + budget, o_sl + budget + 2 * nreq
+    host = torch.empty(total_i32, dtype=torch.int32, pin_memory=True)
+    hv = host.numpy()
+    dev = torch.empty(total_i32, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def gpu_step(sb, evs=None):
+        ns, tq, nc = len(sb.seq_request), int(sb.query_start_loc[-1]), len(sb.copies)
+        hv[o_bt:o_bt + ns * max_blocks] = sb.block_tables.reshape(-1)
+        hv[o_ctx:o_ctx + ns] = sb.context_lens
+        hv[o_qsl:o_qsl + ns + 1] = sb.query_start_loc
+        hv[o_sl:o_sl + tq] = sb.slot_mapping
+        hv[o_cp:o_cp + 2 * nc] = sb.copies.reshape(-1)
+        dev.copy_(host, non_blocking=True)
+        if evs:
+            evs[0].record(stream)
+        if nc:
+            pkv.copy_blocks(kp, vp, dev[o_cp:o_cp + 2 * nc].view(nc, 2))
+        pkv.attention_with_write(
+            qb[:tq], knb[:tq], vnb[:tq], kp, vp, dev[o_sl:o_sl + tq],
+            dev[o_bt:o_bt + ns * max_blocks].view(ns, max_blocks), dev[o_ctx:o_ctx + ns],
+            dev[o_qsl:o_qsl + ns + 1], scale=1.0 / math.sqrt(d),
+            max_context_len=int(sb.context_lens.max()),
+            max_query_len=int(np.diff(sb.query_start_loc).max()), out=out[:tq],
+            workspace=ws)
+        if evs:
+            evs[1].record(stream)
+        torch.cuda.synchronize()
+
+    walls, gpu_ms, steps, tokens = [], [], 0, 0
+    for rep in range(reps + 1):               # the first run warms up
+        alloc, tables, prompt, done = fresh()
+        n_steps = n_tok = 0
+        step_ms = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while done[-1] < prompt[-1]:
+            q = pkv.plan_step(prompt, done, budget)
+            sb = alloc.build_step(tables, done, q, max_blocks)
+            evs = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            gpu_step(sb, evs)
+            step_ms.append(evs[0].elapsed_time(evs[1]))
+            n_steps += 1
+            n_tok += int(sum(q))
+            advance(done, q)
+        wall = time.perf_counter() - t0
+        alloc.close()
+        if rep:
+            walls.append(wall)
+            gpu_ms.append(sum(step_ms) / len(step_ms))
+            steps, tokens = n_steps, n_tok
+    wall = min(walls)
+    del kp, vp, qb, knb, vnb, out, ws, dev
+    torch.cuda.empty_cache()
+    return {"workload": "8,192-token prompt prefilled under a 2,048-token step budget "
+                        "beside 31 decoding requests (contexts U[300,4096]), 16q/8kv "
+                        "heads, d=128, bf16, planned by pkv_plan_step/pkv_build_step",
+            "steps": steps, "tokens": tokens,
+            "host_plan_us_per_step": round(plan_s / nplan * 1e6, 1),
+            "gpu_ms_per_step": round(min(gpu_ms), 5),
+            "wall_ms_per_step": round(wall / steps * 1e3, 5),
+            "wall_ms_total": round(wall * 1e3, 4),
+            "prefill_tokens_per_s": round(plen / wall, 1),
+            "step_tokens_per_s": round(tokens / wall, 1),
+            "wall_includes": "planning, one pinned H2D copy of the step metadata, the "
+                             "fused call, and a host wait per step"}
+
 # ---------------------------------------------------------------------------
 
 def main() -> int:
@@ -409,6 +536,8 @@ def main() -> int:
                     help="only time the prefill chunk of the mixed step (profiling)")
     ap.add_argument("--only-copy", action="store_true",
                     help="only time the copy-on-write block copies (profiling)")
+    ap.add_argument("--only-planned", action="store_true",
+                    help="only time the planner-driven chunked prefill (profiling)")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="(host only) summarise rocprofv3 --pmc runs found in DIR into "
                          "profiles/traffic.json and exit")
@@ -443,6 +572,9 @@ def main() -> int:
 
     if args.only_copy:
         print(json.dumps({"block_copy": measure_block_copy(args.steps)}))
+        return 0
+    if args.only_planned:
+        print(json.dumps({"planned_prefill": measure_planned_prefill()}))
         return 0
     if args.only_chunk:
         print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
@@ -516,6 +648,8 @@ def main() -> int:
         result["workloads"] = extra
         log("timing copy-on-write block copies")
         result["block_copy"] = measure_block_copy(args.steps)
+        log("timing the planner-driven chunked prefill")
+        result["planned_prefill"] = measure_planned_prefill()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -166,7 +166,8 @@ pkv_status paged_attention_varlen_with_write(
  */
 typedef struct pkv_block_allocator pkv_block_allocator;
 
-/* Create an allocator with every block free.  *out receives the handle. */
+/* Create an allocator with every block free (1 <= num_blocks <= INT32_MAX / 16, so
+ * every flat slot fits in int32).  *out receives the handle. */
 pkv_status pkv_allocator_create(int32_t num_blocks, pkv_block_allocator **out);
 void pkv_allocator_destroy(pkv_block_allocator *alloc);
 /* Free blocks (-1 for a NULL handle); reference count of a block (-1 if out of range). */
@@ -220,6 +221,56 @@ pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copie
                                 int32_t num_copies, int32_t num_blocks, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, pkv_dtype dtype,
                                 void *stream);
+
+/*
+ * Step planning for chunked prefill (host only, no device access).
+ * ("How inference engines actually work" page (xiaohu-jiedu), Chunked Prefill
+ * subsection: each step has a token budget, long prompts run as consecutive slices and
+ * the decoding requests' single tokens ride along in every step; serving-engine KV page
+ * (ttlab), section 3, "the new problem": decode tokens fill the step first, and the
+ * per-step token limit counts every token of the step.)
+ *
+ * pkv_plan_step -- how many tokens each of num_requests requests runs this step.
+ *   prompt_len[r], num_computed[r]  host int32: prompt length; tokens whose K/V are
+ *                   cached.  num_computed >= prompt_len > 0 means decoding.
+ *   query_len[r]    host int32, written: 0 = not scheduled.
+ * Decoding requests get 1 token each, in request order, while the budget lasts; the
+ * rest of token_budget goes to requests still prefilling, in request order, each
+ * taking min(prompt_len - num_computed, tokens left).  A zero-length prompt is never
+ * scheduled.  INVALID_ARG for negative sizes or NULL arrays (num_requests > 0).
+ */
+pkv_status pkv_plan_step(int32_t num_requests, const int32_t *prompt_len,
+                         const int32_t *num_computed, int32_t token_budget,
+                         int32_t *query_len);
+
+/*
+ * pkv_build_step -- the varlen batch of one planned step, with its blocks.
+ *   tables        host int32 [num_requests][max_blocks_per_seq], updated in place:
+ *                 each scheduled request's row gains the blocks its new tokens need
+ *                 (and moves to a private copy of a shared, partly filled last block),
+ *                 exactly as pkv_allocator_append does, requests in order.
+ *   num_computed, query_len   host int32 [num_requests] (query_len from pkv_plan_step).
+ * Outputs (host int32; sequence s = the s-th request with query_len > 0):
+ *   seq_request     [num_requests]           request index of sequence s
+ *   block_tables    [num_requests][max_blocks_per_seq]  row s = the request's table,
+ *                   entries past ceil(context_len/16) set to -1
+ *   query_start_loc [num_requests + 1]       prefix sums of the query lengths
+ *   context_lens    [num_requests]           num_computed + query_len
+ *   slot_mapping    [max_tokens]             flat slot of each new token, in batch order
+ *   copies          [num_requests][2]        (source, destination) block copies to run
+ *                                            (paged_kv_copy_blocks) before the write
+ *   *num_seqs, *num_copies
+ * The whole step is checked before anything changes: OUT_OF_BLOCKS if the pool cannot
+ * hold it, INVALID_ARG for bad arguments, a used table entry that is not a held
+ * block, a row that would outgrow max_blocks_per_seq, or more tokens than max_tokens.
+ * On error no table, count or output is changed except *num_seqs = *num_copies = 0.
+ */
+pkv_status pkv_build_step(pkv_block_allocator *alloc, int32_t num_requests, int32_t *tables,
+                          int32_t max_blocks_per_seq, const int32_t *num_computed,
+                          const int32_t *query_len, int32_t *seq_request,
+                          int32_t *block_tables, int32_t *query_start_loc,
+                          int32_t *context_lens, int32_t *slot_mapping, int32_t max_tokens,
+                          int32_t *copies, int32_t *num_seqs, int32_t *num_copies);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *pkv_status_string(pkv_status status);

@@ -43,6 +43,10 @@ SIGNATURES = {
                                             ctypes.POINTER(_i32)]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             ctypes.c_int, _vp]),
+    "pkv_plan_step": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp]),
+    "pkv_build_step": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _i32, _vp, ctypes.POINTER(_i32),
+                                      ctypes.POINTER(_i32)]),
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),

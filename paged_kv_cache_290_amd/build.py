@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip")
+SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip",
+           "planner.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

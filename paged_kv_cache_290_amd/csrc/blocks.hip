@@ -14,8 +14,10 @@
 // Policy choices the pages leave open: the lowest-numbered free block is taken first;
 // an append that does not fit changes nothing; a copy moves whole blocks (every kv
 // head and offset) in both pools.
+#include <limits.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <functional>
 #include <new>
 #include <queue>
@@ -28,16 +30,7 @@
 // host allocator
 // ---------------------------------------------------------------------------
 
-struct pkv_block_allocator {
-  std::vector<int32_t> ref;  // reference count per physical block (0 = free)
-  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_ids;
-};
-
 namespace {
-
-bool valid_held(const pkv_block_allocator *a, int32_t b) {
-  return b >= 0 && b < (int32_t)a->ref.size() && a->ref[b] > 0;
-}
 
 int32_t take(pkv_block_allocator *a) {
   const int32_t b = a->free_ids.top();
@@ -51,6 +44,37 @@ void drop(pkv_block_allocator *a, int32_t b) {
 }
 
 }  // namespace
+
+namespace pkv {
+
+int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context_len,
+                         int32_t num_new, int32_t *slots, int32_t *copies) {
+  const int32_t end = context_len + num_new;
+  const int32_t used = (context_len + kBlock - 1) / kBlock;
+  int32_t ncopy = 0;
+  if (context_len % kBlock != 0 && a->ref[table[used - 1]] > 1) {
+    const int32_t src = table[used - 1];
+    const int32_t dst = take(a);
+    --a->ref[src];  // still held by the other requests
+    table[used - 1] = dst;
+    copies[0] = src;
+    copies[1] = dst;
+    ncopy = 1;
+  }
+  // Slots run block by block: positions [pos, pos + run) share logical block lb.
+  int32_t *out = slots;
+  for (int32_t pos = context_len; pos < end;) {
+    const int32_t lb = pos / kBlock, off = pos % kBlock;
+    if (off == 0) table[lb] = take(a);
+    const int32_t run = std::min<int32_t>(kBlock - off, end - pos);
+    const int32_t base = table[lb] * kBlock + off;
+    for (int32_t i = 0; i < run; ++i) *out++ = base + i;
+    pos += run;
+  }
+  return ncopy;
+}
+
+}  // namespace pkv
 
 // ---------------------------------------------------------------------------
 // block copy kernel: each thread moves 16-byte pieces of (pair, pool) regions
@@ -84,7 +108,8 @@ using namespace pkv;
 extern "C" {
 
 pkv_status pkv_allocator_create(int32_t num_blocks, pkv_block_allocator **out) {
-  if (!out || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  // Flat slots (block * 16 + offset) must fit in int32.
+  if (!out || num_blocks <= 0 || num_blocks > INT32_MAX / kBlock) return PKV_ERR_INVALID_ARG;
   *out = nullptr;
   pkv_block_allocator *a = new (std::nothrow) pkv_block_allocator();
   if (!a) return PKV_ERR_OUT_OF_BLOCKS;
@@ -116,7 +141,7 @@ pkv_status pkv_allocator_fork(pkv_block_allocator *alloc, const int32_t *table,
                               int32_t num_used) {
   if (!alloc || num_used < 0 || (num_used > 0 && !table)) return PKV_ERR_INVALID_ARG;
   for (int32_t i = 0; i < num_used; ++i)
-    if (!valid_held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
+    if (!held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
   for (int32_t i = 0; i < num_used; ++i) ++alloc->ref[table[i]];
   return PKV_OK;
 }
@@ -127,7 +152,7 @@ pkv_status pkv_allocator_release(pkv_block_allocator *alloc, const int32_t *tabl
   // A table naming one block twice would drop it twice: count first, then check.
   std::vector<int32_t> uses;
   for (int32_t i = 0; i < num_used; ++i) {
-    if (!valid_held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
+    if (!held(alloc, table[i])) return PKV_ERR_INVALID_ARG;
   }
   try {
     uses.assign(alloc->ref.size(), 0);
@@ -150,16 +175,15 @@ pkv_status pkv_allocator_append(pkv_block_allocator *alloc, int32_t *table,
     return PKV_ERR_INVALID_ARG;
   if (num_new == 0) return PKV_OK;
   const int64_t end = (int64_t)context_len + num_new;
-  if ((end + kBlock - 1) / kBlock > max_blocks_per_seq) return PKV_ERR_INVALID_ARG;
+  if (end > INT32_MAX || (end + kBlock - 1) / kBlock > max_blocks_per_seq)
+    return PKV_ERR_INVALID_ARG;
   const int32_t used = (context_len + kBlock - 1) / kBlock;
   for (int32_t lb = 0; lb < used; ++lb)
-    if (!valid_held(alloc, table[lb])) return PKV_ERR_INVALID_ARG;
+    if (!held(alloc, table[lb])) return PKV_ERR_INVALID_ARG;
   // What the append needs, before anything changes: a block per 16-token boundary
   // crossed, and a copy of the partly filled last block if it is shared.
-  int64_t need = 0;
+  int64_t need = (end + kBlock - 1) / kBlock - used;
   int32_t ncopy = 0;
-  for (int64_t pos = context_len; pos < end; ++pos)
-    if (pos % kBlock == 0) ++need;
   if (context_len % kBlock != 0 && alloc->ref[table[used - 1]] > 1) {
     ++need;
     ++ncopy;
@@ -167,20 +191,7 @@ pkv_status pkv_allocator_append(pkv_block_allocator *alloc, int32_t *table,
   if (ncopy > max_copies || (ncopy > 0 && !copies)) return PKV_ERR_INVALID_ARG;
   if (need > (int64_t)alloc->free_ids.size()) return PKV_ERR_OUT_OF_BLOCKS;
 
-  if (ncopy) {
-    const int32_t src = table[used - 1];
-    const int32_t dst = take(alloc);
-    --alloc->ref[src];  // still held by the other requests
-    table[used - 1] = dst;
-    copies[0] = src;
-    copies[1] = dst;
-  }
-  for (int64_t pos = context_len; pos < end; ++pos) {
-    const int32_t lb = (int32_t)(pos / kBlock);
-    const int32_t off = (int32_t)(pos % kBlock);
-    if (off == 0) table[lb] = take(alloc);
-    slots[pos - context_len] = table[lb] * kBlock + off;
-  }
+  append_unchecked(alloc, table, context_len, num_new, slots, copies);
   *num_copies = ncopy;
   return PKV_OK;
 }

@@ -6,13 +6,34 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "pagedkv.h"
+
+// Host block allocator state (blocks.hip), also read by the step planner.
+struct pkv_block_allocator {
+  std::vector<int32_t> ref;  // reference count per physical block (0 = free)
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_ids;
+};
 
 namespace pkv {
 
 constexpr int kBlock = PKV_BLOCK_SIZE;  // tokens per physical block
 constexpr int kWaves = 4;               // waves per workgroup in every kernel
 constexpr int kThreads = 64 * kWaves;
+
+// Whether block b is held (reference count > 0) by the allocator.
+inline bool held(const pkv_block_allocator *a, int32_t b) {
+  return b >= 0 && b < (int32_t)a->ref.size() && a->ref[b] > 0;
+}
+
+// The append of pkv_allocator_append after its checks: the caller has verified the
+// table's used entries and that enough blocks are free.  Returns the copies made (0
+// or 1, the pair written to copies[0..1]).
+int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context_len,
+                         int32_t num_new, int32_t *slots, int32_t *copies);
 
 // Decode (single-query rows) plan.
 //

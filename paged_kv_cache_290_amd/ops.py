@@ -5,6 +5,7 @@ computation runs in the library's HIP kernels; nothing here computes.
 from __future__ import annotations
 
 import ctypes
+from typing import NamedTuple
 
 import torch
 
@@ -263,6 +264,79 @@ class BlockAllocator:
         table[:] = [int(x) for x in arr[:end_blocks]]
         pairs = [(int(copies[0]), int(copies[1]))] if ncopy.value else []
         return [int(x) for x in slots[:num_new]], pairs
+
+
+    def build_step(self, tables, num_computed, query_len, max_blocks: int):
+        """The varlen batch of one planned step (pkv_build_step).  `tables` is either a
+        list of per-request block lists or an int32 numpy array [num_requests,
+        max_blocks] (the faster form: passed to the library as is); either is updated
+        in place with the blocks the step needs.  Returns a StepBatch of host int32
+        arrays; nothing changes on error."""
+        import numpy as np
+
+        as_array = isinstance(tables, np.ndarray)
+        n = tables.shape[0] if as_array else len(tables)
+        _require(len(num_computed) == n and len(query_len) == n, "one entry per request")
+        if as_array:
+            _require(tables.dtype == np.int32 and tables.ndim == 2 and
+                     tables.shape[1] == max_blocks and tables.flags.c_contiguous,
+                     "tables must be a C-contiguous int32 [num_requests, max_blocks] array")
+            tab = tables
+        else:
+            tab = np.full((max(n, 1), max_blocks), -1, dtype=np.int32)
+            for r, t in enumerate(tables):
+                _require(len(t) <= max_blocks, f"table {r} longer than max_blocks")
+                tab[r, :len(t)] = t
+        nc = np.ascontiguousarray(num_computed, dtype=np.int32).reshape(-1)
+        ql = np.ascontiguousarray(query_len, dtype=np.int32).reshape(-1)
+        tokens = int(ql.sum()) if n else 0
+        seq_request = np.empty(max(n, 1), dtype=np.int32)
+        bt = np.empty((max(n, 1), max_blocks), dtype=np.int32)
+        qsl = np.empty(n + 1, dtype=np.int32)
+        ctx = np.empty(max(n, 1), dtype=np.int32)
+        slots = np.empty(max(tokens, 1), dtype=np.int32)
+        copies = np.empty((max(n, 1), 2), dtype=np.int32)
+        ns, ncp = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = self._lib.pkv_build_step(self._h, n, tab.ctypes.data, max_blocks,
+                                      nc.ctypes.data, ql.ctypes.data, seq_request.ctypes.data,
+                                      bt.ctypes.data, qsl.ctypes.data, ctx.ctypes.data,
+                                      slots.ctypes.data, tokens, copies.ctypes.data,
+                                      ctypes.byref(ns), ctypes.byref(ncp))
+        _lib.check("pkv_build_step", st)
+        if not as_array:
+            for r in range(n):
+                if ql[r] > 0:
+                    tables[r][:] = tab[r, :(int(nc[r]) + int(ql[r]) + 15) // 16].tolist()
+        s = ns.value
+        if n == 0:
+            qsl[0] = 0
+        return StepBatch(seq_request[:s], bt[:s], qsl[:s + 1], ctx[:s], slots[:tokens],
+                         copies[:ncp.value])
+
+
+class StepBatch(NamedTuple):
+    """Host int32 metadata of one engine step (pkv_build_step's outputs)."""
+    seq_request: "np.ndarray"      # request index of each sequence
+    block_tables: "np.ndarray"     # [num_seqs, max_blocks], -1 past the used blocks
+    query_start_loc: "np.ndarray"  # [num_seqs + 1]
+    context_lens: "np.ndarray"     # [num_seqs]
+    slot_mapping: "np.ndarray"     # [total new tokens]
+    copies: "np.ndarray"           # [num_copies, 2] (source, destination)
+
+
+def plan_step(prompt_len, num_computed, token_budget: int) -> list:
+    """Tokens each request runs this step under `token_budget` (pkv_plan_step): decode
+    tokens first, then prompt slices in request order."""
+    import numpy as np
+
+    pl = np.asarray(prompt_len, dtype=np.int32).reshape(-1)
+    nc = np.asarray(num_computed, dtype=np.int32).reshape(-1)
+    _require(pl.shape == nc.shape, "prompt_len and num_computed differ in length")
+    ql = np.zeros(max(len(pl), 1), dtype=np.int32)
+    st = _lib.load().pkv_plan_step(len(pl), pl.ctypes.data, nc.ctypes.data, token_budget,
+                                   ql.ctypes.data)
+    _lib.check("pkv_plan_step", st)
+    return [int(x) for x in ql[:len(pl)]]
 
 
 def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, copies: torch.Tensor,
