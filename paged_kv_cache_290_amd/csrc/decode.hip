@@ -252,7 +252,10 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   if (T_all == 0) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep everything
+  // derived from it (block range, loop bounds, buffer descriptors) in scalar registers
+  // instead of wrapping each buffer load in a loop over distinct descriptor values.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = lane % CPR;
   const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
   const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   constexpr bool kF32 = std::is_same<T, float>::value;
   constexpr int DW = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (gw >= p.items * p.groups * HG) return;
   const int hh = gw % HG;
   const int seg = gw / HG;
@@ -704,10 +707,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   const int h = kvh * group + (g - kvh * p.num_head_groups) * HG + hh;
   const size_t base = (size_t)first * HG + hh;  // slot of piece i: base + i * HG
 
-  // One pass in batches of 8 pieces (indices past the end are clamped to the last
+  // One pass in batches of 16 pieces (indices past the end are clamped to the last
   // piece and weighted 0): each batch's lse and o values are loaded together, and the
   // running sums are rescaled when the running maximum rises.
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   float M = -INFINITY, L = 0.f;
   float o[DW];
 #pragma unroll
