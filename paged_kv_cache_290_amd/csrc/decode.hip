@@ -35,6 +35,11 @@
 
 namespace pkv {
 
+// Set-up cost of a segment (query load, flush of a partial) for the static split of the
+// work, in K/V bytes streamed in the same time: measured best at 4-6 blocks of 4 KiB
+// (d=64 bf16) and ~2 blocks of 8 KiB (d=128 bf16).
+constexpr int kSegCostBytes = 20 * 1024;
+
 constexpr float kRescaleSlack = 8.0f;
 
 // Lane mapping for one (block, kv head) tile of 16 tokens x D elements, row R bytes.
@@ -178,6 +183,9 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   using M = DecodeMap<T, D>;
   constexpr int CPR = M::CPR, TPI = M::TPI, NV = M::NV, EPC = M::EPC, WPC = M::WPC;
   constexpr int kTileBytes = kBlock * D * (int)sizeof(T);
+  // Segment set-up cost in blocks (one block = a K tile and a V tile).
+  constexpr int kSegCost =
+      kSegCostBytes / (2 * kTileBytes) > 1 ? kSegCostBytes / (2 * kTileBytes) : 1;
 
   __shared__ int s_pref[kMaxStreamItems + 1];
   __shared__ int s_keys[kMaxStreamItems];
@@ -217,9 +225,29 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_row, s_seq, s_tmp);
   const int rows_total = s_pref[p.items];
   const int64_t T_all = (int64_t)rows_total * p.groups;
-  // With fewer blocks than waves only the first T_all waves work, so every working
-  // wave owns at least one block.
+  // With fewer blocks than waves only the first T_all waves work.
   const int W = (int)min<int64_t>((int64_t)gridDim.x * kWaves, T_all);
+  // The static split balances cost, not blocks: each segment costs its blocks plus
+  // kSegCost block-equivalents of set-up (query load, a partial's flush), so a wave
+  // whose range crosses segment starts gets fewer blocks.  In cost order a segment
+  // (g, item) starts at g*rows_cost + s_pref[item] + kSegCost*item, and its block lb
+  // sits at that start + kSegCost + lb.  Wave w owns the cost range
+  // [w*T_cost/W, (w+1)*T_cost/W); its blocks stay one contiguous run in block order.
+  const int64_t rows_cost = (int64_t)rows_total + (int64_t)kSegCost * p.items;
+  const int64_t T_cost = rows_cost * p.groups;
+  auto wave_of_cost = [&](int64_t c) { return (int)(((c + 1) * W - 1) / T_cost); };
+  // Blocks (in block order) whose cost position is below c.
+  auto blocks_before = [&](int64_t c) -> int64_t {
+    const int64_t g = c / rows_cost;
+    const int64_t cc = c - g * rows_cost;
+    int lo = 0, hi = p.items - 1;  // last item whose cost start is <= cc
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] + (int64_t)kSegCost * mid <= cc) lo = mid; else hi = mid - 1;
+    }
+    const int64_t off = cc - (s_pref[lo] + (int64_t)kSegCost * lo);
+    return g * rows_total + s_pref[lo] + (off > kSegCost ? off - kSegCost : 0);
+  };
   if (blockIdx.x == 0) {
     // Rows of sequences that break q_len <= context_len: defined as zeros.
     for (int i = threadIdx.x; i < p.items; i += kThreads) {
@@ -236,10 +264,10 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       const int item = sg - g * p.items;
       int first = 0, pieces = 0;
       if (s_pref[item + 1] > s_pref[item]) {
-        const int64_t s0 = (int64_t)g * rows_total + s_pref[item];
-        const int64_t s1 = s0 + (s_pref[item + 1] - s_pref[item]);
-        const int w0 = (int)(((s0 + 1) * W - 1) / T_all);
-        const int w1 = (int)((s1 * W - 1) / T_all);
+        const int64_t c0 = (int64_t)g * rows_cost + s_pref[item] + (int64_t)kSegCost * item +
+                           kSegCost;  // cost position of the segment's first block
+        const int w0 = wave_of_cost(c0);
+        const int w1 = wave_of_cost(c0 + (s_pref[item + 1] - s_pref[item]) - 1);
         if (w1 > w0) {
           first = sg + w0;
           pieces = w1 - w0 + 1;
@@ -260,8 +288,10 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
   const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (w >= W) return;
-  const int64_t wb0 = (int64_t)w * T_all / W;  // the wave's blocks: [wb0, wb0 + nbw)
-  const int nbw = (int)((int64_t)(w + 1) * T_all / W - wb0);
+  // The wave's blocks: [wb0, wb0 + nbw) in block order (possibly none).
+  const int64_t wb0 = blocks_before((int64_t)w * T_cost / W);
+  const int nbw = (int)(blocks_before((int64_t)(w + 1) * T_cost / W) - wb0);
+  if (nbw == 0) return;
   const int group = a.num_q_heads / a.num_kv_heads;
   const char *kpool = static_cast<const char *>(a.k_pool);
   const char *vpool = static_cast<const char *>(a.v_pool);
