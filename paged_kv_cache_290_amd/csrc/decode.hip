@@ -235,15 +235,32 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   // [w*T_cost/W, (w+1)*T_cost/W); its blocks stay one contiguous run in block order.
   const int64_t rows_cost = (int64_t)rows_total + (int64_t)kSegCost * p.items;
   const int64_t T_cost = rows_cost * p.groups;
-  auto wave_of_cost = [&](int64_t c) { return (int)(((c + 1) * W - 1) / T_cost); };
-  // Blocks (in block order) whose cost position is below c.
+  // Every product and quotient below fits in 31 bits for all but huge batches; then
+  // the divisions run in 32-bit arithmetic (64-bit division is a long instruction
+  // sequence on the GPU, and these sit on the path to the first block).
+  const bool narrow = T_cost * (int64_t)(W + 1) < (int64_t)INT32_MAX;
+  auto quot = [narrow](int64_t x, int64_t y) -> int64_t {
+    return narrow ? (int64_t)((uint32_t)x / (uint32_t)y) : x / y;
+  };
+  auto wave_of_cost = [&](int64_t c) { return (int)quot((c + 1) * W - 1, T_cost); };
+  // Blocks (in block order) whose cost position is below c (c wave-uniform).  The
+  // item holding c is found with one LDS read and a ballot when there are at most 64
+  // items (lane i tests item i), else by binary search.
   auto blocks_before = [&](int64_t c) -> int64_t {
-    const int64_t g = c / rows_cost;
+    const int64_t g = quot(c, rows_cost);
     const int64_t cc = c - g * rows_cost;
-    int lo = 0, hi = p.items - 1;  // last item whose cost start is <= cc
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] + (int64_t)kSegCost * mid <= cc) lo = mid; else hi = mid - 1;
+    int lo;  // last item whose cost start is <= cc (item 0 starts at 0)
+    if (p.items <= 64) {
+      const int ln = threadIdx.x & 63;
+      const bool le = ln < p.items && s_pref[ln] + (int64_t)kSegCost * ln <= cc;
+      lo = 63 - __builtin_clzll(__builtin_amdgcn_ballot_w64(le));
+    } else {
+      lo = 0;
+      int hi = p.items - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] + (int64_t)kSegCost * mid <= cc) lo = mid; else hi = mid - 1;
+      }
     }
     const int64_t off = cc - (s_pref[lo] + (int64_t)kSegCost * lo);
     return g * rows_total + s_pref[lo] + (off > kSegCost ? off - kSegCost : 0);
@@ -289,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (w >= W) return;
   // The wave's blocks: [wb0, wb0 + nbw) in block order (possibly none).
-  const int64_t wb0 = blocks_before((int64_t)w * T_cost / W);
-  const int nbw = (int)(blocks_before((int64_t)(w + 1) * T_cost / W) - wb0);
+  const int64_t wb0 = blocks_before(quot((int64_t)w * T_cost, W));
+  const int nbw = (int)(blocks_before(quot((int64_t)(w + 1) * T_cost, W)) - wb0);
   if (nbw == 0) return;
   const int group = a.num_q_heads / a.num_kv_heads;
   const char *kpool = static_cast<const char *>(a.k_pool);
@@ -395,15 +412,31 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
     // physical block (invalid table entries read block 0 and are masked).  All table
     // entries of the chunk are fetched at once, whatever pieces the chunk spans.
     int m_g = 0, m_item = 0, m_lb = 0, m_pb = 0, m_ok = 0, m_keys = 0;
-    if (lane < nc) {
-      const int64_t bi = wb0 + c0 + lane;
-      m_g = (int)(bi / rows_total);
-      const int r = (int)(bi - (int64_t)m_g * rows_total);
-      int lo = 0, hi = p.items - 1;  // last item with s_pref[item] <= r
+    // Item of the chunk's first block (last item with s_pref[item] <= r): a ballot
+    // over lanes for up to 64 items, else a binary search.  Each lane then walks
+    // forward from it to its own block's item; a chunk spans few items, and a lane
+    // already in the next kv-head group starts from item 0 near that group's start.
+    const int64_t b_first = wb0 + c0;
+    const int g_first = (int)quot(b_first, rows_total);
+    const int r_first = (int)(b_first - (int64_t)g_first * rows_total);
+    int it0;
+    if (p.items <= 64) {
+      it0 = 63 - __builtin_clzll(
+                     __builtin_amdgcn_ballot_w64(lane < p.items && s_pref[lane] <= r_first));
+    } else {
+      int lo = 0, hi = p.items - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] <= r) lo = mid; else hi = mid - 1;
+        if (s_pref[mid] <= r_first) lo = mid; else hi = mid - 1;
       }
+      it0 = lo;
+    }
+    if (lane < nc) {
+      const int64_t bi = wb0 + c0 + lane;
+      m_g = (int)quot(bi, rows_total);
+      const int r = (int)(bi - (int64_t)m_g * rows_total);
+      int lo = m_g == g_first ? it0 : 0;  // last item with s_pref[item] <= r
+      while (lo + 1 < p.items && s_pref[lo + 1] <= r) ++lo;
       m_item = lo;
       m_lb = r - s_pref[lo];
       m_keys = s_keys[lo];
