@@ -540,6 +540,93 @@ def measure_planned_prefill(reps: int = 3) -> dict:
             "wall_includes": "planning, one pinned H2D copy of the step metadata, the "
                              "fused call, and a host wait per step"}
 
+
+def measure_prefix_cache(calls: int = 20) -> dict:
+    """Prefix caching on the serving-engine page's measurement shape: a 3,000-token
+    common prefix plus a 32-token tail per request (Qwen3-1.7B heads 16q/8kv, d=128,
+    bf16).  Host: the block keys of one 3,032-token prompt (pkv_block_keys, SHA-256)
+    and the cache lookup of a later request (pkv_prefix_match, 187 blocks found).
+    GPU: the attention prefill of the whole prompt (the first request) against that of
+    the 40 tokens a later request still computes (HIP events per call, calls queued
+    behind a spin kernel)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_290_amd as pkv
+
+    hq, hkv, d, nb, mb = 16, 8, 128, 1024, 256
+    rng = np.random.Generator(np.random.PCG64(0))
+    prefix = [int(x) for x in rng.integers(0, 151_936, 3000)]
+    prompts = [prefix + [int(x) for x in rng.integers(0, 151_936, 32)] for _ in range(8)]
+
+    t0 = time.perf_counter()
+    for p in prompts:
+        pkv.block_keys(p)
+    key_us = (time.perf_counter() - t0) / len(prompts) * 1e6
+    alloc = pkv.BlockAllocator(nb)
+    alloc.enable_prefix_cache()
+    first = []
+    alloc.append(first, 0, len(prompts[0]))
+    alloc.prefix_register(first, pkv.block_keys(prompts[0]))
+    match_us, tables, hits = 0.0, [], 0
+    for p in prompts[1:]:
+        keys = pkv.block_keys(p)
+        t0 = time.perf_counter()
+        t = alloc.prefix_match(keys)
+        match_us += time.perf_counter() - t0
+        hits = len(t)
+        alloc.append(t, 16 * len(t), len(p) - 16 * len(t))
+        tables.append(t)
+    match_us = match_us / (len(prompts) - 1) * 1e6
+
+    kp = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa
+    stream = torch.cuda.current_stream()
+
+    def timed(table, ctx, n):
+        q = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda").normal_()
+        kn = torch.empty((n, hkv, d), dtype=torch.bfloat16, device="cuda").normal_()
+        vn = torch.empty_like(kn).normal_()
+        slots = i32([table[p // 16] * 16 + p % 16 for p in range(ctx - n, ctx)])
+        bt = np.full((1, mb), -1, np.int32)
+        bt[0, :len(table)] = table
+        bt, cl, qsl = i32(bt), i32([ctx]), i32([0, n])
+        ws = torch.empty(pkv.workspace_size(1, n, hq, hkv, d, ctx, torch.bfloat16) or 1,
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+
+        def call():
+            pkv.attention_with_write(q, kn, vn, kp, vp, slots, bt, cl, qsl,
+                                     scale=1.0 / math.sqrt(d), max_context_len=ctx,
+                                     max_query_len=n, out=out, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        torch.cuda._sleep(int(1e8))
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / calls
+
+    ctx = len(prompts[0])
+    full_ms = timed(first, ctx, ctx)
+    tail_ms = timed(tables[0], ctx, ctx - 16 * hits)
+    del kp, vp
+    torch.cuda.empty_cache()
+    return {"workload": "3,000-token common prefix + 32-token tail per request, 16q/8kv "
+                        "heads, d=128, bf16",
+            "host_block_keys_us_per_prompt": round(key_us, 1),
+            "host_hash_MBps": round((ctx // 16) * (32 + 64 + 4) / key_us, 1),
+            "host_match_us": round(match_us, 2), "blocks_found": hits,
+            "tokens_prefilled_first": ctx, "tokens_prefilled_later": ctx - 16 * hits,
+            "gpu_prefill_first_ms": round(full_ms, 5),
+            "gpu_prefill_later_ms": round(tail_ms, 5),
+            "prefill_speedup": round(full_ms / tail_ms, 2)}
+
 # ---------------------------------------------------------------------------
 
 def main() -> int:
@@ -557,6 +644,8 @@ def main() -> int:
                     help="only time the prefill chunk of the mixed step (profiling)")
     ap.add_argument("--only-copy", action="store_true",
                     help="only time the copy-on-write block copies (profiling)")
+    ap.add_argument("--only-prefix", action="store_true",
+                    help="only time prefix caching (host keys and lookup, GPU prefill)")
     ap.add_argument("--only-planned", action="store_true",
                     help="only time the planner-driven chunked prefill (profiling)")
     ap.add_argument("--write-traffic", metavar="DIR",
@@ -596,6 +685,9 @@ def main() -> int:
         return 0
     if args.only_planned:
         print(json.dumps({"planned_prefill": measure_planned_prefill()}))
+        return 0
+    if args.only_prefix:
+        print(json.dumps({"prefix_cache": measure_prefix_cache()}))
         return 0
     if args.only_chunk:
         print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
@@ -671,6 +763,8 @@ def main() -> int:
         result["block_copy"] = measure_block_copy(args.steps)
         log("timing the planner-driven chunked prefill")
         result["planned_prefill"] = measure_planned_prefill()
+        log("timing prefix caching")
+        result["prefix_cache"] = measure_prefix_cache()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

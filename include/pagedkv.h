@@ -223,6 +223,62 @@ pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copie
                                 void *stream);
 
 /*
+ * Prefix caching (host only).  (Serving-engine KV page (ttlab), section 4 "prefix
+ * cache": a key per full block hashed from the previous block's key, the block's token
+ * ids and extra inputs, SHA-256; freed blocks keep their contents in an eviction
+ * queue, entered tail first and evicted least recently used first.  Inference-engine
+ * page (xiaohu-jiedu), agent-traffic section: a request whose prefix matches points
+ * its table at the blocks already in memory, so only its new tail is prefilled.)
+ */
+#define PKV_KEY_BYTES 32
+
+/*
+ * pkv_block_keys -- keys of the full blocks of a token sequence (host arrays).
+ *   tokens[num_tokens]  int32 token ids; block b = tokens[16b .. 16b+15]
+ *   extras[extras_len]  bytes hashed into every key (adapter id, multimodal hashes,
+ *                       cache salt); may be NULL when extras_len == 0
+ *   parent_key          32 bytes: key of the block before tokens[0], or NULL at the
+ *                       start of a sequence (then 32 zero bytes)
+ *   keys                [max_keys][32] out: key b = SHA-256(key b-1 || the 16 ids as
+ *                       little-endian int32 || extras_len as little-endian uint32 ||
+ *                       extras); *num_keys = num_tokens / 16 (a partial block has none)
+ * INVALID_ARG if max_keys < num_tokens / 16 or an argument is missing.
+ */
+pkv_status pkv_block_keys(const int32_t *tokens, int32_t num_tokens, const void *extras,
+                          int32_t extras_len, const uint8_t *parent_key, uint8_t *keys,
+                          int32_t max_keys, int32_t *num_keys);
+
+/*
+ * pkv_allocator_enable_prefix_cache -- from now on, a block whose last reference goes
+ * keeps its content if it was registered (it becomes evictable instead of free).  A
+ * new block is a free one (lowest id first) while any is left, else the least
+ * recently used evictable one, whose key is then forgotten.  pkv_allocator_num_free
+ * counts free plus evictable blocks, and pkv_allocator_release drops a table's
+ * blocks last first, so a finished request's tail is evicted before its head.
+ */
+pkv_status pkv_allocator_enable_prefix_cache(pkv_block_allocator *alloc);
+
+/*
+ * pkv_prefix_match -- the longest run of leading keys[0..num_keys) that are cached:
+ * their blocks go to table[0..*num_hit) and each gains a reference (an evictable one
+ * leaves the eviction queue).  The request then has *num_hit * 16 tokens cached.
+ */
+pkv_status pkv_prefix_match(pkv_block_allocator *alloc, const uint8_t *keys, int32_t num_keys,
+                            int32_t *table, int32_t *num_hit);
+
+/*
+ * pkv_prefix_register -- cache the FULL held blocks table[i] under keys[i], i <
+ * num_keys (call once their K/V are written).  A key already cached keeps its block;
+ * a block already cached keeps its key.  INVALID_ARG if a block is not held.
+ */
+pkv_status pkv_prefix_register(pkv_block_allocator *alloc, const int32_t *table,
+                               const uint8_t *keys, int32_t num_keys);
+
+/* Cached blocks (held or evictable) and evictable blocks; -1 for a NULL handle. */
+int32_t pkv_prefix_num_cached(const pkv_block_allocator *alloc);
+int32_t pkv_prefix_num_evictable(const pkv_block_allocator *alloc);
+
+/*
  * Step planning for chunked prefill (host only, no device access).
  * ("How inference engines actually work" page (xiaohu-jiedu), Chunked Prefill
  * subsection: each step has a token budget, long prompts run as consecutive slices and

@@ -43,6 +43,13 @@ SIGNATURES = {
                                             ctypes.POINTER(_i32)]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             ctypes.c_int, _vp]),
+    "pkv_block_keys": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _i32,
+                                      ctypes.POINTER(_i32)]),
+    "pkv_allocator_enable_prefix_cache": (ctypes.c_int, [_vp]),
+    "pkv_prefix_match": (ctypes.c_int, [_vp, _vp, _i32, _vp, ctypes.POINTER(_i32)]),
+    "pkv_prefix_register": (ctypes.c_int, [_vp, _vp, _vp, _i32]),
+    "pkv_prefix_num_cached": (_i32, [_vp]),
+    "pkv_prefix_num_evictable": (_i32, [_vp]),
     "pkv_plan_step": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp]),
     "pkv_build_step": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i32, _vp, ctypes.POINTER(_i32),

@@ -74,6 +74,33 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
   return p;
 }
 
+PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+                         int head_dim, int max_context_len, pkv_dtype dtype,
+                         size_t ws_offset) {
+  PrefillPlan p{};
+  const int group = num_q_heads / num_kv_heads;
+  p.head_group = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  p.num_head_groups = group / p.head_group;
+  p.tile_slots = prefill_tile_slots(total_q, num_seqs, kPrefillCols / p.head_group);
+  p.tiles = p.tile_slots * num_kv_heads * p.num_head_groups;
+  // Split the key range when the tiles cannot fill the compute units, keeping at
+  // least two 128-key steps per split.
+  const int cus = device_cus();
+  const int steps = (max_context_len + 127) / 128;
+  p.splits = 1;
+  if (dtype == PKV_BF16 && p.tiles > 0 && p.tiles < cus && steps >= 4)
+    p.splits = std::max(1, std::min((cus + p.tiles - 1) / p.tiles, steps / 2));
+  p.ws_end = ws_offset;
+  if (p.splits > 1) {
+    const size_t parts = (size_t)p.tiles * p.splits * kPrefillCols;
+    p.ws_o_offset = align256(ws_offset);
+    p.ws_lse_offset = p.ws_o_offset + align256(parts * head_dim * sizeof(float));
+    p.ws_col_offset = p.ws_lse_offset + align256(parts * sizeof(float));
+    p.ws_end = p.ws_col_offset + align256((size_t)p.tiles * kPrefillCols * sizeof(int));
+  }
+  return p;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -114,9 +141,13 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t
       num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype) ||
       max_context_len < 0)
     return 0;
-  return plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                     max_context_len, dtype)
-      .ws_bytes;
+  // Decode partials first, then the partials of split prefill chunks.
+  const size_t dec = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                 max_context_len, dtype)
+                         .ws_bytes;
+  return plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                      max_context_len, dtype, dec)
+      .ws_end;
 }
 
 }  // extern "C"
@@ -150,9 +181,13 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
 
   DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                 max_context_len, dtype);
-  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
-    return PKV_ERR_WORKSPACE;
+  PrefillPlan pplan = plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                   max_context_len, dtype, plan.ws_bytes);
+  const bool chunks_planned = dtype == PKV_BF16 && max_query_len > 1;
+  const size_t need = chunks_planned ? pplan.ws_end : plan.ws_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   plan.workspace = workspace;
+  pplan.workspace = workspace;
 
   AttnArgs a{};
   a.out = out;
@@ -192,7 +227,7 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
     }
   }
   if (e == hipSuccess && decode_rows) e = launch_decode(a, plan, dtype, st);
-  if (e == hipSuccess && chunks) e = launch_prefill(a, dtype, st);
+  if (e == hipSuccess && chunks) e = launch_prefill(a, pplan, dtype, st);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -32,15 +32,31 @@
 
 namespace {
 
+// A free block (lowest id first); with none left, the least recently used evictable
+// cached block, whose key is forgotten.
 int32_t take(pkv_block_allocator *a) {
-  const int32_t b = a->free_ids.top();
-  a->free_ids.pop();
+  int32_t b;
+  if (!a->free_ids.empty()) {
+    b = a->free_ids.top();
+    a->free_ids.pop();
+  } else {
+    b = a->lru_head;
+    pkv::lru_unlink(a, b);
+    pkv::forget_key(a, b);
+  }
   a->ref[b] = 1;
   return b;
 }
 
+// One reference fewer; a block with none left keeps its content (most recently used
+// end of the eviction list) if it is cached, else becomes free.
 void drop(pkv_block_allocator *a, int32_t b) {
-  if (--a->ref[b] == 0) a->free_ids.push(b);
+  if (--a->ref[b] == 0) {
+    if (a->prefix && a->has_key[b])
+      pkv::lru_push_back(a, b);
+    else
+      a->free_ids.push(b);
+  }
 }
 
 }  // namespace
@@ -129,7 +145,7 @@ pkv_status pkv_allocator_create(int32_t num_blocks, pkv_block_allocator **out) {
 void pkv_allocator_destroy(pkv_block_allocator *alloc) { delete alloc; }
 
 int32_t pkv_allocator_num_free(const pkv_block_allocator *alloc) {
-  return alloc ? (int32_t)alloc->free_ids.size() : -1;
+  return alloc ? (int32_t)available(alloc) : -1;
 }
 
 int32_t pkv_allocator_refcount(const pkv_block_allocator *alloc, int32_t block) {
@@ -161,7 +177,8 @@ pkv_status pkv_allocator_release(pkv_block_allocator *alloc, const int32_t *tabl
   }
   for (int32_t i = 0; i < num_used; ++i)
     if (++uses[table[i]] > alloc->ref[table[i]]) return PKV_ERR_INVALID_ARG;
-  for (int32_t i = 0; i < num_used; ++i) drop(alloc, table[i]);
+  // Tail first: a finished request's last blocks enter the eviction list first.
+  for (int32_t i = num_used - 1; i >= 0; --i) drop(alloc, table[i]);
   return PKV_OK;
 }
 
@@ -189,7 +206,7 @@ pkv_status pkv_allocator_append(pkv_block_allocator *alloc, int32_t *table,
     ++ncopy;
   }
   if (ncopy > max_copies || (ncopy > 0 && !copies)) return PKV_ERR_INVALID_ARG;
-  if (need > (int64_t)alloc->free_ids.size()) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > available(alloc)) return PKV_ERR_OUT_OF_BLOCKS;
 
   append_unchecked(alloc, table, context_len, num_new, slots, copies);
   *num_copies = ncopy;

@@ -8,14 +8,35 @@
 
 #include <functional>
 #include <queue>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
 
-// Host block allocator state (blocks.hip), also read by the step planner.
+// Host block allocator state (blocks.hip, prefix.hip), also read by the step planner.
+// A block with no references is either free (no content kept; in free_ids) or, with
+// the prefix cache enabled, evictable (its cached content kept; in the LRU list).
+struct pkv_block_key {
+  uint64_t w[4];  // the 32 key bytes
+  bool operator==(const pkv_block_key &o) const {
+    return w[0] == o.w[0] && w[1] == o.w[1] && w[2] == o.w[2] && w[3] == o.w[3];
+  }
+};
+struct pkv_block_key_hash {
+  size_t operator()(const pkv_block_key &k) const { return (size_t)k.w[0]; }
+};
 struct pkv_block_allocator {
-  std::vector<int32_t> ref;  // reference count per physical block (0 = free)
+  std::vector<int32_t> ref;  // reference count per physical block
   std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_ids;
+  // Prefix cache (off until enabled): key per cached block, the key -> block map, and
+  // the evictable blocks as a doubly linked list in least-recently-used order.
+  bool prefix = false;
+  std::vector<uint8_t> has_key;
+  std::vector<pkv_block_key> key;
+  std::unordered_map<pkv_block_key, int32_t, pkv_block_key_hash> block_of;
+  std::vector<int32_t> lru_prev, lru_next;  // -1 = none; membership: in_lru
+  std::vector<uint8_t> in_lru;
+  int32_t lru_head = -1, lru_tail = -1, lru_count = 0;
 };
 
 namespace pkv {
@@ -28,6 +49,16 @@ constexpr int kThreads = 64 * kWaves;
 inline bool held(const pkv_block_allocator *a, int32_t b) {
   return b >= 0 && b < (int32_t)a->ref.size() && a->ref[b] > 0;
 }
+
+// Blocks that can be handed out: free ones plus evictable cached ones.
+inline int64_t available(const pkv_block_allocator *a) {
+  return (int64_t)a->free_ids.size() + a->lru_count;
+}
+
+// Eviction-list and key bookkeeping of the prefix cache (prefix.hip).
+void lru_unlink(pkv_block_allocator *a, int32_t b);
+void lru_push_back(pkv_block_allocator *a, int32_t b);
+void forget_key(pkv_block_allocator *a, int32_t b);
 
 // The append of pkv_allocator_append after its checks: the caller has verified the
 // table's used entries and that enough blocks are free.  Returns the copies made (0
@@ -99,7 +130,32 @@ hipError_t launch_kv_write(const void *k_new, const void *v_new, void *k_pool,
 hipError_t launch_decode(const AttnArgs &a, const DecodePlan &p, pkv_dtype dtype,
                          hipStream_t stream);
 
-hipError_t launch_prefill(const AttnArgs &a, pkv_dtype dtype, hipStream_t stream);
+// Prefill (chunk) plan.  A workgroup owns kPrefillCols (query row, q head) columns of
+// one KV head; with fewer tiles than compute units the key range of each tile is split
+// over `splits` workgroups whose partial results a merge kernel combines.
+constexpr int kPrefillCols = 128;
+struct PrefillPlan {
+  int head_group;       // q heads per tile (4, 2 or 1)
+  int num_head_groups;  // G / head_group
+  int tile_slots;       // tile slots per (kv head, head group)
+  int tiles;            // tile_slots * num_kv_heads * num_head_groups
+  int splits;           // key-range splits per tile (1 = none)
+  size_t ws_o_offset, ws_lse_offset, ws_col_offset, ws_end;  // ws_end: bytes used
+  void *workspace;      // set by the caller before launching
+};
+// Partial-result buffers of a split launch (unused when splits == 1).
+struct PrefillSplit {
+  int splits;
+  float *o;    // [tile][split][column][D] normalised partial outputs
+  float *lse;  // [tile][split][column] log2-sum-exp (-inf: no key seen)
+  int *col;    // [tile][column] output row index (row * Hq + head), -1 = unused
+};
+
+PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
+                         int head_dim, int max_context_len, pkv_dtype dtype,
+                         size_t ws_offset);
+hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &p, pkv_dtype dtype,
+                          hipStream_t stream);
 
 // Work-slot count of the prefill launch: an upper bound on the number of query tiles
 // over all sequences (each sequence's tiles fit between floor(qsl[s]/BM) + s and the

@@ -97,7 +97,7 @@ pkv_status pkv_build_step(pkv_block_allocator *alloc, int32_t num_requests, int3
     }
   }
   if (tokens > max_tokens) return PKV_ERR_INVALID_ARG;
-  if (need > (int64_t)alloc->free_ids.size()) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > pkv::available(alloc)) return PKV_ERR_OUT_OF_BLOCKS;
 
   int32_t s = 0, t = 0, nc = 0;
   query_start_loc[0] = 0;

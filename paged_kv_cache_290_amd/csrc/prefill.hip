@@ -47,7 +47,7 @@ namespace {
 constexpr int kPThreads = 512;  // 8 waves
 constexpr int kHalfKeys = 64;   // keys per wave group per step
 constexpr int kStepKeys = 128;  // keys per step
-constexpr int kCols = 128;      // columns per workgroup
+constexpr int kCols = kPrefillCols;  // columns per workgroup
 constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
 constexpr uint32_t kBf16Ones = 0x3F803F80u;  // two bf16 1.0
@@ -180,7 +180,8 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint2 *vb,
 template <int D, int HGP>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                                                                  int num_head_groups,
-                                                                 int tile_slots) {
+                                                                 int tile_slots,
+                                                                 PrefillSplit ps) {
   constexpr int BMQ = kCols / HGP;  // query rows per workgroup
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
@@ -205,9 +206,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  const int total = tile_slots * a.num_kv_heads * num_head_groups;
+  const int total = tile_slots * a.num_kv_heads * num_head_groups * ps.splits;
   int v = xcd_remap(blockIdx.x, total);
   if (v >= total) return;
+  // The splits of one tile are consecutive workgroups (one XCD, shared K/V in its L2).
+  const int split = v % ps.splits;
+  v /= ps.splits;
+  const int tile = v;
+  const int tid = threadIdx.x;
+  // Split partials: until this tile's columns are known, mark them all unused, so the
+  // merge skips tiles that end early (decode rows, empty slots, broken lengths).
+  if (ps.splits > 1 && split == 0 && tid < kCols) ps.col[(size_t)tile * kCols + tid] = -1;
   const int slot = v % tile_slots;
   v /= tile_slots;
   const int hgi = v % num_head_groups;
@@ -282,7 +291,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int pos_first = ctx - q_len + qi0;
   const int ctx_eff = min(ctx, a.max_blocks_per_seq * kBlock);
   const int kv_end = min(pos_first + nq, ctx_eff);
-  const int nst = (kv_end + kStepKeys - 1) / kStepKeys;
+  const int nst_tile = (kv_end + kStepKeys - 1) / kStepKeys;
+  // This split's steps [st0, nst) of the tile's nst_tile (the split-K of short chunks
+  // over long contexts; one split covers them all otherwise).
+  const int st0 = (int)((int64_t)split * nst_tile / ps.splits);
+  const int nst = (int)((int64_t)(split + 1) * nst_tile / ps.splits);
   const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
   const uint16_t *kpool = static_cast<const uint16_t *>(a.k_pool);
   const uint16_t *vpool = static_cast<const uint16_t *>(a.v_pool);
@@ -299,7 +312,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   // Block-table entries of the keys this workgroup reads, cached in LDS kTblCache at a
   // time (refilled every kTblCache/8 steps); invalid entries read block 0.
   const int nblk = (kv_end + kBlock - 1) / kBlock;
-  const int tid = threadIdx.x;
 #define PKV_FILL_TBL(first_blk)                                                          \
   do {                                                                                   \
     if (tid < kTblCache) {                                                               \
@@ -395,12 +407,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     }                                                                                    \
   } while (0)
 
-  PKV_FILL_TBL(0);
+  PKV_FILL_TBL((st0 * (kStepKeys / kBlock)) / kTblCache * kTblCache);
   __syncthreads();
-  if (nst > 0) {
-    PKV_FETCH(0);
-    PKV_MASK_REGS(0);
-    PKV_STAGE(0);
+  if (ps.splits > 1 && split == 0) {  // after the unused marks: a barrier lies between
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+      if (half == 0 && lg == 0 && col_ok[cg])
+        ps.col[(size_t)tile * kCols + cw * 32 + cg * 16 + l16] =
+            col_row[cg] * a.num_q_heads + col_head[cg];
+  }
+  if (st0 < nst) {
+    PKV_FETCH(st0);
+    PKV_MASK_REGS(st0);
+    PKV_STAGE(st0 & 1);
   }
   __syncthreads();
   // Retire every outstanding load (the query fragments in particular) on all paths
@@ -409,7 +428,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   // prefetch as well, which undoes the overlap.
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int st = 0; st < nst; ++st) {
+  for (int st = st0; st < nst; ++st) {
     const int buf = st & 1;
     // Refill the table cache before the first fetch that needs new entries.
     if (st + 1 < nst && ((st + 1) * (kStepKeys / kBlock)) % kTblCache == 0) {
@@ -469,6 +488,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     const float L = a0 * lsum[cg] + a1 * l1;
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     if (!col_ok[cg]) continue;
+    if (ps.splits > 1) {
+      // This split's normalised output and log2-sum-exp (-inf when it saw no key).
+      const size_t pc = ((size_t)tile * ps.splits + split) * kCols + cw * 32 + cg * 16 + l16;
+      float *po = ps.o + pc * D;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4 y;
+        y.x = (a0 * o[mt][cg][0] + a1 * xch[((mt * 2 + cg) * 4 + 0) * 64]) * inv;
+        y.y = (a0 * o[mt][cg][1] + a1 * xch[((mt * 2 + cg) * 4 + 1) * 64]) * inv;
+        y.z = (a0 * o[mt][cg][2] + a1 * xch[((mt * 2 + cg) * 4 + 2) * 64]) * inv;
+        y.w = (a0 * o[mt][cg][3] + a1 * xch[((mt * 2 + cg) * 4 + 3) * 64]) * inv;
+        *reinterpret_cast<float4 *>(po + mt * 16 + 4 * lg) = y;
+      }
+      if (lg == 0) ps.lse[pc] = L > 0.f ? mx + __builtin_amdgcn_logf(L) : -INFINITY;
+      continue;
+    }
     uint16_t *dst = out + ((size_t)col_row[cg] * a.num_q_heads + col_head[cg]) * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -489,30 +524,81 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 #undef PKV_MASK_REGS
 #undef PKV_STAGE
 
+// Log-sum-exp merge of the splits of each tile column: out = sum_s 2^(lse_s - M) o_s /
+// sum_s 2^(lse_s - M), M = max_s lse_s.  Each thread owns four dims of one column
+// (D/4 threads per column), so a tile spreads over kCols*D/4/256 workgroups.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a, PrefillSplit ps) {
+  constexpr int TPC = D / 4;      // threads per column
+  constexpr int CPW = 256 / TPC;  // columns per workgroup
+  constexpr int WPT = kCols / CPW;  // workgroups per tile
+  const int tile = blockIdx.x / WPT;
+  const int c = (blockIdx.x % WPT) * CPW + threadIdx.x / TPC;
+  const int d0 = (threadIdx.x % TPC) * 4;
+  const int dst = ps.col[(size_t)tile * kCols + c];
+  if (dst < 0) return;
+  const size_t base = (size_t)tile * ps.splits * kCols + c;  // column c of split 0
+  float M = -INFINITY;
+  for (int s = 0; s < ps.splits; ++s) M = fmaxf(M, ps.lse[base + (size_t)s * kCols]);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s = 0; s < ps.splits; ++s) {
+      const size_t ps_ = base + (size_t)s * kCols;
+      const float ls = ps.lse[ps_];
+      const float4 x = *reinterpret_cast<const float4 *>(ps.o + ps_ * D + d0);
+      const float w = ls == -INFINITY ? 0.f : fast_exp2(ls - M);
+      L += w;
+      acc.x = fmaf(w, x.x, acc.x);
+      acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z);
+      acc.w = fmaf(w, x.w, acc.w);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint2 packed;
+  packed.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  packed.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + (size_t)dst * D + d0) = packed;
+}
+
 template <int D, int HGP>
-static hipError_t launch_prefill_t(const AttnArgs &a, hipStream_t st) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int nhg = group / HGP;
-  const int slots = prefill_tile_slots(a.total_q, a.num_seqs, kCols / HGP);
-  const int total = slots * a.num_kv_heads * nhg;
+static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, hipStream_t st) {
+  const int total = pl.tiles * pl.splits;
   if (total == 0) return hipSuccess;
+  PrefillSplit ps{};
+  ps.splits = pl.splits;
+  if (pl.splits > 1) {
+    char *w = static_cast<char *>(pl.workspace);
+    ps.o = reinterpret_cast<float *>(w + pl.ws_o_offset);
+    ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
+    ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
+  }
   const int grid = ((total + 7) / 8) * 8;
-  prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kPThreads), 0, st>>>(a, nhg, slots);
+  prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kPThreads), 0, st>>>(a, pl.num_head_groups,
+                                                                       pl.tile_slots, ps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.splits == 1) return e;
+  prefill_merge_kernel<D><<<dim3(pl.tiles * (kCols * D / 4 / 256)), dim3(256), 0, st>>>(a, ps);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t st) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<D, 4>(a, st);
-  if (group % 2 == 0) return launch_prefill_t<D, 2>(a, st);
-  return launch_prefill_t<D, 1>(a, st);
+static hipError_t launch_prefill_d(const AttnArgs &a, const PrefillPlan &pl, hipStream_t st) {
+  switch (pl.head_group) {
+    case 4: return launch_prefill_t<D, 4>(a, pl, st);
+    case 2: return launch_prefill_t<D, 2>(a, pl, st);
+    case 1: return launch_prefill_t<D, 1>(a, pl, st);
+  }
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const AttnArgs &a, pkv_dtype dtype, hipStream_t stream) {
+hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &pl, pkv_dtype dtype,
+                          hipStream_t stream) {
   if (dtype != PKV_BF16) return hipErrorInvalidValue;
-  if (a.head_dim == 64) return launch_prefill_d<64>(a, stream);
-  if (a.head_dim == 128) return launch_prefill_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, stream);
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, stream);
   return hipErrorInvalidValue;
 }
 

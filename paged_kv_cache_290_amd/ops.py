@@ -314,6 +314,43 @@ class BlockAllocator:
                          copies[:ncp.value])
 
 
+    # ---- prefix cache ----
+    def enable_prefix_cache(self) -> None:
+        """Keep the contents of registered blocks after their last reference goes
+        (pkv_allocator_enable_prefix_cache)."""
+        _lib.check("pkv_allocator_enable_prefix_cache",
+                   self._lib.pkv_allocator_enable_prefix_cache(self._h))
+
+    def prefix_match(self, keys: list) -> list:
+        """Blocks of the longest cached run of leading keys (each gains a reference)."""
+        import numpy as np
+
+        n = len(keys)
+        kb = np.frombuffer(b"".join(keys), dtype=np.uint8) if n else np.zeros(1, np.uint8)
+        table = np.zeros(max(n, 1), dtype=np.int32)
+        hit = ctypes.c_int32(0)
+        _lib.check("pkv_prefix_match", self._lib.pkv_prefix_match(
+            self._h, kb.ctypes.data, n, table.ctypes.data, ctypes.byref(hit)))
+        return [int(x) for x in table[:hit.value]]
+
+    def prefix_register(self, table: list, keys: list) -> None:
+        """Cache the full blocks table[i] under keys[i] (pkv_prefix_register)."""
+        import numpy as np
+
+        n = min(len(table), len(keys))
+        if n == 0:
+            return
+        t = np.asarray(table[:n], dtype=np.int32)
+        kb = np.frombuffer(b"".join(keys[:n]), dtype=np.uint8)
+        _lib.check("pkv_prefix_register", self._lib.pkv_prefix_register(
+            self._h, t.ctypes.data, kb.ctypes.data, n))
+
+    def num_cached(self) -> int:
+        return int(self._lib.pkv_prefix_num_cached(self._h))
+
+    def num_evictable(self) -> int:
+        return int(self._lib.pkv_prefix_num_evictable(self._h))
+
 class StepBatch(NamedTuple):
     """Host int32 metadata of one engine step (pkv_build_step's outputs)."""
     seq_request: "np.ndarray"      # request index of each sequence
@@ -323,6 +360,23 @@ class StepBatch(NamedTuple):
     slot_mapping: "np.ndarray"     # [total new tokens]
     copies: "np.ndarray"           # [num_copies, 2] (source, destination)
 
+
+def block_keys(tokens, extras: bytes = b"", parent: bytes | None = None) -> list:
+    """32-byte keys of the full blocks of `tokens` (pkv_block_keys)."""
+    import numpy as np
+
+    t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    n = len(t) // BLOCK_SIZE
+    out = np.zeros(max(n, 1) * 32, dtype=np.uint8)
+    ex = np.frombuffer(extras, dtype=np.uint8) if extras else None
+    pk = np.frombuffer(parent, dtype=np.uint8) if parent is not None else None
+    _require(parent is None or len(parent) == 32, "parent key must be 32 bytes")
+    got = ctypes.c_int32(0)
+    _lib.check("pkv_block_keys", _lib.load().pkv_block_keys(
+        t.ctypes.data if len(t) else None, len(t),
+        ex.ctypes.data if ex is not None else None, len(extras),
+        pk.ctypes.data if pk is not None else None, out.ctypes.data, n, ctypes.byref(got)))
+    return [out[32 * i:32 * (i + 1)].tobytes() for i in range(got.value)]
 
 def plan_step(prompt_len, num_computed, token_budget: int) -> list:
     """Tokens each request runs this step under `token_budget` (pkv_plan_step): decode
