@@ -627,6 +627,57 @@ def measure_prefix_cache(calls: int = 20) -> dict:
             "gpu_prefill_later_ms": round(tail_ms, 5),
             "prefill_speedup": round(full_ms / tail_ms, 2)}
 
+
+def measure_swap(calls: int = 10, n: int = 1024) -> dict:
+    """KV swap of n Qwen3-1.7B-shaped blocks (8 kv heads x 16 x 128 bf16: 32 KiB per
+    block and pool, 64 MiB for n = 1,024) to pinned host memory and back, each call
+    timed with HIP events; beside them, plain pinned copies of the same size in each
+    direction (the host link's practical limit on this machine)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_290_amd as pkv
+
+    hkv, d, nb = 8, 128, 4 * n
+    rng = np.random.Generator(np.random.PCG64(0))
+    kp = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    blocks = torch.from_numpy(rng.permutation(nb)[:n].astype(np.int32)).cuda()
+    nbytes = pkv.swap_bytes(kp, n)
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    staging = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / calls
+
+    out_ms = timed(lambda: pkv.swap_out(kp, vp, blocks, staging, host))
+    in_ms = timed(lambda: pkv.swap_in(kp, vp, blocks, staging, host))
+    d2h_ms = timed(lambda: host.copy_(dev, non_blocking=True))
+    h2d_ms = timed(lambda: dev.copy_(host, non_blocking=True))
+    gb = nbytes / 1e9
+    del kp, vp, staging, dev
+    torch.cuda.empty_cache()
+    return {"workload": f"{n} blocks of 8 kv heads x 16 x 128 bf16, both pools "
+                        f"({nbytes / 2**20:.0f} MiB), pinned host memory",
+            "swap_out_ms": round(out_ms, 4), "swap_in_ms": round(in_ms, 4),
+            "swap_out_GBs": round(gb / (out_ms * 1e-3), 2),
+            "swap_in_GBs": round(gb / (in_ms * 1e-3), 2),
+            "plain_d2h_GBs": round(gb / (d2h_ms * 1e-3), 2),
+            "plain_h2d_GBs": round(gb / (h2d_ms * 1e-3), 2),
+            "swap_out_frac_of_link": round(d2h_ms / out_ms, 3),
+            "swap_in_frac_of_link": round(h2d_ms / in_ms, 3)}
+
 # ---------------------------------------------------------------------------
 
 def main() -> int:
@@ -644,6 +695,8 @@ def main() -> int:
                     help="only time the prefill chunk of the mixed step (profiling)")
     ap.add_argument("--only-copy", action="store_true",
                     help="only time the copy-on-write block copies (profiling)")
+    ap.add_argument("--only-swap", action="store_true",
+                    help="only time the KV swap to host memory and back")
     ap.add_argument("--only-prefix", action="store_true",
                     help="only time prefix caching (host keys and lookup, GPU prefill)")
     ap.add_argument("--only-planned", action="store_true",
@@ -688,6 +741,9 @@ def main() -> int:
         return 0
     if args.only_prefix:
         print(json.dumps({"prefix_cache": measure_prefix_cache()}))
+        return 0
+    if args.only_swap:
+        print(json.dumps({"swap": measure_swap()}))
         return 0
     if args.only_chunk:
         print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
@@ -765,6 +821,8 @@ def main() -> int:
         result["planned_prefill"] = measure_planned_prefill()
         log("timing prefix caching")
         result["prefix_cache"] = measure_prefix_cache()
+        log("timing KV swap")
+        result["swap"] = measure_swap()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -328,6 +328,36 @@ pkv_status pkv_build_step(pkv_block_allocator *alloc, int32_t num_requests, int3
                           int32_t *context_lens, int32_t *slot_mapping, int32_t max_tokens,
                           int32_t *copies, int32_t *num_seqs, int32_t *num_copies);
 
+/*
+ * KV swap between the pools and host memory.  ("How inference engines actually work"
+ * page (xiaohu-jiedu), agent-traffic section: a request idle during a tool call has
+ * its KV cache moved to CPU memory and moved back for its next turn; serving-engine
+ * KV page (ttlab), section 5: preemption, dropping the KV and prefilling again, is
+ * the alternative.)
+ *
+ * Host image of n blocks: the K rows of blocks[0..n) then their V rows, each block
+ * as it lies in a pool (num_kv_heads*16*head_dim elements); paged_kv_swap_bytes(n,
+ * ...) bytes.  `staging` is a DEVICE buffer of the same size (caller-owned).  `host`
+ * should be pinned (hipHostMalloc) for the copy to be asynchronous; it must stay
+ * valid and, for a swap-in, unmodified until `stream` has passed the call.
+ *   blocks  int32 [n] DEVICE array of physical block ids; an id outside [0,
+ *           num_blocks) gathers zeros (swap-out) or is skipped (swap-in).
+ * Swap-out: gathers the blocks into staging, then one device-to-host copy.  The
+ * blocks may be reused once the copy has been issued (stream order).  Swap-in: one
+ * host-to-device copy into staging, then a scatter into the (typically different)
+ * blocks.  n == 0 is a no-op.  Asynchronous on `stream`.
+ */
+size_t paged_kv_swap_bytes(int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, pkv_dtype dtype);
+pkv_status paged_kv_swap_out(const void *k_pool, const void *v_pool, const int32_t *blocks,
+                             int32_t n, void *staging, void *host, int32_t num_blocks,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             pkv_dtype dtype, void *stream);
+pkv_status paged_kv_swap_in(void *k_pool, void *v_pool, const int32_t *blocks, int32_t n,
+                            void *staging, const void *host, int32_t num_blocks,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            pkv_dtype dtype, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *pkv_status_string(pkv_status status);
 

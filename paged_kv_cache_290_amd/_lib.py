@@ -54,6 +54,11 @@ SIGNATURES = {
     "pkv_build_step": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i32, _vp, ctypes.POINTER(_i32),
                                       ctypes.POINTER(_i32)]),
+    "paged_kv_swap_bytes": (_sz, [_i32, _i32, _i32, _i32, ctypes.c_int]),
+    "paged_kv_swap_out": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, ctypes.c_int, _vp]),
+    "paged_kv_swap_in": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                        _i32, ctypes.c_int, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),

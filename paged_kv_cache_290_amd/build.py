@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip",
-           "planner.hip", "prefix.hip")
+           "planner.hip", "prefix.hip", "swap.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

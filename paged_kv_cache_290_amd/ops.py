@@ -361,6 +361,53 @@ class StepBatch(NamedTuple):
     copies: "np.ndarray"           # [num_copies, 2] (source, destination)
 
 
+def swap_bytes(k_pool: torch.Tensor, n: int) -> int:
+    """Bytes of the host image (and staging buffer) of n blocks of these pools."""
+    nb, hkv, bs, d = k_pool.shape
+    return int(_lib.load().paged_kv_swap_bytes(n, hkv, d, bs, _dtype_code(k_pool)))
+
+
+def _swap_args(k_pool, v_pool, blocks, staging, host, n_bytes):
+    dev = k_pool.device
+    for nme, t in (("k_pool", k_pool), ("v_pool", v_pool), ("blocks", blocks),
+                   ("staging", staging)):
+        _on_gpu(nme, t, dev)
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    _require(blocks.dtype == torch.int32 and blocks.dim() == 1, "blocks must be int32 [n]")
+    _require(host.device.type == "cpu" and host.is_contiguous(), "host must be a CPU tensor")
+    _require(staging.is_contiguous(), "staging must be contiguous")
+    _require(host.numel() * host.element_size() >= n_bytes and
+             staging.numel() * staging.element_size() >= n_bytes,
+             "host and staging must hold swap_bytes(k_pool, n) bytes")
+
+
+def swap_out(k_pool: torch.Tensor, v_pool: torch.Tensor, blocks: torch.Tensor,
+             staging: torch.Tensor, host: torch.Tensor, stream=None) -> None:
+    """Copy blocks (device int32 [n]) of both pools to `host` (pinned CPU tensor, K then
+    V) through the device `staging` buffer (paged_kv_swap_out)."""
+    n = blocks.shape[0]
+    _swap_args(k_pool, v_pool, blocks, staging, host, swap_bytes(k_pool, n))
+    nb, hkv, bs, d = k_pool.shape
+    st = _lib.load().paged_kv_swap_out(k_pool.data_ptr(), v_pool.data_ptr(),
+                                       blocks.data_ptr(), n, staging.data_ptr(),
+                                       host.data_ptr(), nb, hkv, d, bs, _dtype_code(k_pool),
+                                       _stream_handle(stream))
+    _lib.check("paged_kv_swap_out", st)
+
+
+def swap_in(k_pool: torch.Tensor, v_pool: torch.Tensor, blocks: torch.Tensor,
+            staging: torch.Tensor, host: torch.Tensor, stream=None) -> None:
+    """Write the host image back into blocks (device int32 [n]) of both pools
+    (paged_kv_swap_in)."""
+    n = blocks.shape[0]
+    _swap_args(k_pool, v_pool, blocks, staging, host, swap_bytes(k_pool, n))
+    nb, hkv, bs, d = k_pool.shape
+    st = _lib.load().paged_kv_swap_in(k_pool.data_ptr(), v_pool.data_ptr(),
+                                      blocks.data_ptr(), n, staging.data_ptr(),
+                                      host.data_ptr(), nb, hkv, d, bs, _dtype_code(k_pool),
+                                      _stream_handle(stream))
+    _lib.check("paged_kv_swap_in", st)
+
 def block_keys(tokens, extras: bytes = b"", parent: bytes | None = None) -> list:
     """32-byte keys of the full blocks of `tokens` (pkv_block_keys)."""
     import numpy as np
