@@ -257,10 +257,14 @@ def cpu_baseline(b, budget_s: float = 10.0) -> dict:
 # counters taken offline (profiles/traffic.json), valid only for unchanged kernels
 # ---------------------------------------------------------------------------
 
+# The sources that define the decode call whose HBM traffic the counters measure.
+TRAFFIC_SOURCES = ("api.hip", "decode.hip", "pkv_device.h", "pkv_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_290_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in TRAFFIC_SOURCES:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()
