@@ -560,8 +560,9 @@ def measure_prefix_cache(calls: int = 20) -> dict:
 
     hq, hkv, d, nb, mb = 16, 8, 128, 1024, 256
     rng = np.random.Generator(np.random.PCG64(0))
-    prefix = [int(x) for x in rng.integers(0, 151_936, 3000)]
-    prompts = [prefix + [int(x) for x in rng.integers(0, 151_936, 32)] for _ in range(8)]
+    prefix = rng.integers(0, 151_936, 3000).astype(np.int32)
+    prompts = [np.concatenate([prefix, rng.integers(0, 151_936, 32).astype(np.int32)])
+               for _ in range(8)]
 
     t0 = time.perf_counter()
     for p in prompts:
@@ -625,6 +626,7 @@ def measure_prefix_cache(calls: int = 20) -> dict:
                         "heads, d=128, bf16",
             "host_block_keys_us_per_prompt": round(key_us, 1),
             "host_hash_MBps": round((ctx // 16) * (32 + 64 + 4) / key_us, 1),
+            "host_keys_via": "binding, int32 token array in",
             "host_match_us": round(match_us, 2), "blocks_found": hits,
             "tokens_prefilled_first": ctx, "tokens_prefilled_later": ctx - 16 * hits,
             "gpu_prefill_first_ms": round(full_ms, 5),

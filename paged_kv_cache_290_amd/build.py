@@ -20,7 +20,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip",
            "planner.hip", "prefix.hip", "swap.hip")
+# Host-only C++ (no device code), compiled by the host compiler.
+HOST_SOURCES = ("sha256_x86.cpp",)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for the device code (the host pass
@@ -51,6 +54,11 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".host.o"))
+        objs.append(obj)
+        cmds.append([CXX, "-O3", "-std=c++17", "-fPIC", "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"

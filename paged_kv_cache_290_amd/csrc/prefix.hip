@@ -21,6 +21,12 @@
 
 #include "pkv_internal.h"
 
+namespace pkv {
+// SHA-256 compression with the x86 SHA extensions (sha256_x86.cpp, host compiler).
+bool sha256_x86_available();
+void sha256_x86_chunks(uint32_t h[8], const uint8_t *data, size_t nchunks);
+}  // namespace pkv
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -67,8 +73,16 @@ void sha256_chunk(uint32_t h[8], const uint8_t *p) {
 void sha256(const uint8_t *msg, size_t len, uint8_t out[32]) {
   uint32_t h[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
                    0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
-  size_t off = 0;
-  for (; off + 64 <= len; off += 64) sha256_chunk(h, msg + off);
+  static const bool x86 = pkv::sha256_x86_available();
+  auto chunks = [&](const uint8_t *p, size_t n) {
+    if (x86) {
+      pkv::sha256_x86_chunks(h, p, n);
+    } else {
+      for (size_t i = 0; i < n; ++i) sha256_chunk(h, p + 64 * i);
+    }
+  };
+  size_t off = len / 64 * 64;
+  chunks(msg, len / 64);
   // Final chunk(s): the rest, 0x80, zeros, the bit length as a big-endian uint64.
   uint8_t tail[128] = {0};
   const size_t rest = len - off;
@@ -77,7 +91,7 @@ void sha256(const uint8_t *msg, size_t len, uint8_t out[32]) {
   const size_t tl = rest + 9 <= 64 ? 64 : 128;
   const uint64_t bits = (uint64_t)len * 8;
   for (int i = 0; i < 8; ++i) tail[tl - 1 - i] = (uint8_t)(bits >> (8 * i));
-  for (size_t o = 0; o < tl; o += 64) sha256_chunk(h, tail + o);
+  chunks(tail, tl / 64);
   for (int i = 0; i < 8; ++i) {
     out[4 * i] = (uint8_t)(h[i] >> 24);
     out[4 * i + 1] = (uint8_t)(h[i] >> 16);

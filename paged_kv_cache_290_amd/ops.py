@@ -423,7 +423,8 @@ def block_keys(tokens, extras: bytes = b"", parent: bytes | None = None) -> list
         t.ctypes.data if len(t) else None, len(t),
         ex.ctypes.data if ex is not None else None, len(extras),
         pk.ctypes.data if pk is not None else None, out.ctypes.data, n, ctypes.byref(got)))
-    return [out[32 * i:32 * (i + 1)].tobytes() for i in range(got.value)]
+    raw = out.tobytes()
+    return [raw[32 * i:32 * i + 32] for i in range(got.value)]
 
 def plan_step(prompt_len, num_computed, token_budget: int) -> list:
     """Tokens each request runs this step under `token_budget` (pkv_plan_step): decode
