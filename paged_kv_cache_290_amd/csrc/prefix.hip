@@ -15,6 +15,7 @@
 // previous key (32 bytes, all zero before the first block), the 16 token ids as
 // little-endian int32, the extras length as little-endian uint32, the extras bytes.
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -73,7 +74,8 @@ void sha256_chunk(uint32_t h[8], const uint8_t *p) {
 void sha256(const uint8_t *msg, size_t len, uint8_t out[32]) {
   uint32_t h[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
                    0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
-  static const bool x86 = pkv::sha256_x86_available();
+  // PKV_SHA256_PORTABLE=1 forces the portable rounds (the tests check both paths).
+  static const bool x86 = pkv::sha256_x86_available() && !getenv("PKV_SHA256_PORTABLE");
   auto chunks = [&](const uint8_t *p, size_t n) {
     if (x86) {
       pkv::sha256_x86_chunks(h, p, n);

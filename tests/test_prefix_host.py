@@ -173,3 +173,24 @@ def test_prefix_errors():
     assert a.num_cached() == 2 and a.prefix_match(keys) == t
     with pytest.raises(ValueError):
         block_keys(list(range(32)), parent=b"short")
+
+
+def test_portable_sha256_path_matches_oracle():
+    """The portable SHA-256 rounds (used where the host CPU lacks the SHA extensions),
+    forced in a fresh process, give the same keys as hashlib."""
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np, oracle.prefix_oracle as P, paged_kv_cache_290_amd as pkv\n"
+        "rng = np.random.Generator(np.random.PCG64(9))\n"
+        "for n, e in ((0, 0), (16, 0), (200, 3), (333, 40)):\n"
+        "    t = [int(x) for x in rng.integers(0, 2**31 - 1, n)]\n"
+        "    ex = bytes(range(e))\n"
+        "    assert pkv.block_keys(t, ex) == P.block_keys(t, ex), (n, e)\n"
+        "print('ok')\n")
+    import os
+    env = dict(os.environ, PKV_SHA256_PORTABLE="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], env=env, cwd=root,
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stderr
