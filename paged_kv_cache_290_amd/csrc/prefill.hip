@@ -64,6 +64,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) {
   return __builtin_bit_cast(bf16x8_t, x);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land at LDS
+// byte address lds_byte + 16*L (lds_byte is wave-uniform; it travels in M0).  Written
+// as asm so that the compiler, which cannot tell the two LDS buffers apart, does not
+// hold this step's LDS reads until the next step's loads have landed; the kernel waits
+// for these loads itself (vmcnt) before the barrier that publishes the buffer.
+__device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_byte) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_byte));
+}
+
 // One wave's update with a 64-key tile: kb = K tile [key][chunk ^ key%NCH], vb = V^T
 // tile [dim][16-byte unit ^ dim%8] (two 4-key groups per unit); kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
@@ -338,9 +347,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const uint32_t blk_bytes = (uint32_t)a.num_kv_heads * kBlock * D * 2;
   const int kch = tid % NCH;
   const int kkey0 = tid / NCH;
+  // K goes from global memory straight into LDS: one wave's 16-byte loads land at
+  // consecutive LDS addresses (lane L at 16*L), i.e. rows kw0 + L/NCH, slot L%NCH, so
+  // a lane fetches the chunk that the row's swizzle puts in its slot.  The row's
+  // residue mod NCH is that of kkey0 for every i (KSTRIDE is a multiple of NCH).
+  const int kw0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (64 / NCH);
   const char *kthr = reinterpret_cast<const char *>(kpool) +
-                     (((size_t)kvh * kBlock + kkey0 % kBlock) * D + kch * 8) * 2;
-  uint4 kreg[KCH];
+                     (((size_t)kvh * kBlock + kkey0 % kBlock) * D +
+                      (kch ^ (kkey0 % NCH)) * 8) * 2;
   uint4 vreg[4];
   const bool vtask = tid < 2 * VTH;
   const int vhalf = tid / VTH;
@@ -354,12 +368,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int vpair_h = (vkg / 4) % 2;
   const char *vthr = reinterpret_cast<const char *>(vpool) +
                      (((size_t)kvh * kBlock + 4 * (vkg % 4)) * D + vj * 8) * 2;
-#define PKV_FETCH(st)                                                                    \
+#define PKV_FETCH(st, buf)                                                               \
   do {                                                                                   \
     const int b0_ = ((st) * (kStepKeys / kBlock)) % kTblCache;                           \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
       const uint32_t blk_ = (uint32_t)s_tbl[b0_ + (kkey0 + KSTRIDE * i) / kBlock];       \
-      kreg[i] = *reinterpret_cast<const uint4 *>(kthr + (uint64_t)blk_ * blk_bytes);     \
+      const int key_ = kw0 + KSTRIDE * i;                                                \
+      load_lds16(kthr + (uint64_t)blk_ * blk_bytes,                                      \
+                 (uint32_t)(uintptr_t)(k_lds + ((buf) * 2 + key_ / kHalfKeys) * K_U4 +     \
+                                       (key_ % kHalfKeys) * NCH));                       \
     }                                                                                    \
     if (vtask) {                                                                         \
       const uint32_t blk_ = (uint32_t)s_tbl[b0_ + vblk];                                 \
@@ -373,8 +390,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   do {                                                                                   \
     const int k0_ = (st) * kStepKeys;                                                    \
     if (k0_ + kStepKeys > kv_end) {                                                      \
-      _Pragma("unroll") for (int i = 0; i < KCH; ++i) if (k0_ + kkey0 + KSTRIDE * i >=   \
-                                                            kv_end) kreg[i] = uint4{};   \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) if (k0_ + kHalfKeys * vhalf +        \
                                                         4 * vkg + i >= kv_end)           \
           vreg[i] = uint4{};                                                             \
@@ -382,12 +397,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   } while (0)
 #define PKV_STAGE(buf)                                                                   \
   do {                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const int key = kkey0 + KSTRIDE * i;                                               \
-      const int kh = key / kHalfKeys;                                                    \
-      const int kl = key % kHalfKeys;                                                    \
-      k_lds[((buf) * 2 + kh) * K_U4 + kl * NCH + (kch ^ (kl % NCH))] = kreg[i];          \
-    }                                                                                    \
     if (vtask) {                                                                         \
       uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2 + vpair_h;                        \
       const uint32_t w_[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},           \
@@ -417,10 +426,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
             col_row[cg] * a.num_q_heads + col_head[cg];
   }
   if (st0 < nst) {
-    PKV_FETCH(st0);
+    PKV_FETCH(st0, st0 & 1);
     PKV_MASK_REGS(st0);
     PKV_STAGE(st0 & 1);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // K landed in LDS (the loads write it directly)
   __syncthreads();
   // Retire every outstanding load (the query fragments in particular) on all paths
   // here.  Otherwise the wait counters merged at the loop head still see the query
@@ -435,7 +445,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       PKV_FILL_TBL((st + 1) * (kStepKeys / kBlock));
       __syncthreads();
     }
-    if (st + 1 < nst) PKV_FETCH(st + 1);  // in flight while this step is computed
+    if (st + 1 < nst) PKV_FETCH(st + 1, buf ^ 1);  // in flight during this step
 
     const int kbase = st * kStepKeys + half * kHalfKeys;
     if (kbase < kv_end) {
@@ -453,6 +463,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       PKV_MASK_REGS(st + 1);
       PKV_STAGE(buf ^ 1);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // step st+1's K has landed in LDS
     __syncthreads();  // step st+1 staged; everyone is done reading step st
   }
 
