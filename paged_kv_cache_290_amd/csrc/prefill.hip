@@ -73,12 +73,22 @@ __device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_byte) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_byte));
 }
 
-// One wave's update with a 64-key tile: kb = K tile [key][chunk ^ key%NCH], vb = V^T
-// tile [dim][16-byte unit ^ dim%8] (two 4-key groups per unit); kbase = position of the tile's first key.  MASK
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+
+// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16; lane mapping
+// stated where it is used).
+__device__ __forceinline__ v4i16_t lds_read_tr16(const void *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t *)(p));
+}
+
+// One wave's update with a 64-key tile: kb and vb = K and V tiles, each row-major
+// [key][16-byte chunk ^ key%NCH]; kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
 // position or past kv_end).
 template <int D, bool MASK>
-__device__ __forceinline__ void tile_update(const uint4 *kb, const uint2 *vb,
+__device__ __forceinline__ void tile_update(const uint4 *kb, const uint4 *vb,
                                             const bf16x8_t (&qf)[2][D / 32],
                                             f32x4_t (&o)[D / 16][2], float (&mref)[2],
                                             float (&mneg)[2], float (&lsum)[2], float sc,
@@ -170,14 +180,26 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint2 *vb,
   }
 
   // O^T += V^T P^T: A row = dim, k-slots (lg, e) <-> keys 32*ks2 + 4*lg + e (e < 4)
-  // and 32*ks2 + 16 + 4*lg + (e - 4), matching the slots of pf.
-  const uint4 *vb4 = reinterpret_cast<const uint4 *>(vb);
+  // and 32*ks2 + 16 + 4*lg + (e - 4), matching the slots of pf.  Each half of an A
+  // fragment is one transposing LDS read (ds_read_b64_tr_b16): within a 16-lane group
+  // g, lane i receives element i%4 of the 4-element rows addressed by lanes
+  // 16g + 4j + i/4, j = 0..3.  So lane (g, j = l16/4, q = l16%4) addresses dims
+  // 16*mt + 4q..4q+3 of key 4g + j (+16 for the second half), and lane (g, i) receives
+  // dim 16*mt + i of keys 4g + 0..3.
+  const int vj = l16 >> 2;
+  const int vq = l16 & 3;
+  const int vkey = 4 * lg + vj;
+  const int vsw = (vq >> 1) ^ (vkey % NCH);  // chunk of dims 16*mt + 4q is 2mt + q/2
+  const char *vrow = reinterpret_cast<const char *>(vb) + vkey * (NCH * 16) + (vq & 1) * 8;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int dim = mt * 16 + l16;
+    const char *vp = vrow + ((2 * mt) ^ vsw) * 16;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const bf16x8_t af = as_bf16x8(vb4[dim * 8 + ((4 * ks2 + lg) ^ (dim & 7))]);
+      const v4i16_t lo = lds_read_tr16(vp + (32 * ks2) * (NCH * 16));
+      const v4i16_t hi = lds_read_tr16(vp + (32 * ks2 + 16) * (NCH * 16));
+      const bf16x8_t af = __builtin_bit_cast(
+          bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) o[mt][cg] = mfma16(af, pf[cg][ks2], o[mt][cg]);
     }
@@ -195,18 +217,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
   constexpr int NCH = D / 8;        // 16-byte chunks per K row
-  constexpr int K_U4 = kHalfKeys * NCH;               // uint4 per K tile
-  constexpr int V_U2 = D * (kHalfKeys / 4);           // uint2 per V^T tile (4 keys each)
-  constexpr int KCH = kStepKeys * NCH / kPThreads;    // K chunks per thread per step
-  constexpr int VTH = 16 * NCH;                       // (4-key group, chunk) tasks per half
-  constexpr int LDS_U4 = 4 * K_U4 + 2 * V_U2;         // [buf][half] K tiles, then V^T
+  constexpr int K_U4 = kHalfKeys * NCH;               // uint4 per K (or V) tile
+  constexpr int KCH = kStepKeys * NCH / kPThreads;    // chunks per thread per step, each pool
+  constexpr int LDS_U4 = 8 * K_U4;                    // [buf][half] K tiles, then V tiles
   constexpr int XF = MT * 8 + 4;                      // floats per lane in the merge
   static_assert(4 * XF * 64 * 4 <= LDS_U4 * 16, "merge exchange must fit the tiles");
-  static_assert(2 * VTH <= kPThreads, "one V task per thread at most");
   __shared__ uint4 lds[LDS_U4];
   __shared__ int s_tbl[kTblCache];  // block-table entries of this workgroup
-  uint4 *const k_lds = lds;                                       // [buf*2+half][K_U4]
-  uint2 *const vt_lds = reinterpret_cast<uint2 *>(lds + 4 * K_U4);  // [buf*2+half][V_U2]
+  uint4 *const k_lds = lds;             // [buf*2+half][K_U4]
+  uint4 *const v_lds = lds + 4 * K_U4;  // [buf*2+half][K_U4]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -330,88 +349,51 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     }                                                                                    \
   } while (0)
 
-  // Staging of a 128-key step.  fetch: global -> registers, every load unconditional:
-  // a key past kv_end reads a row of its block, or of block 0 when its table entry
-  // is past the sequence (the cache holds 0 there), and is zeroed when staged, so all
-  // of a step's loads leave back to back.  stage: registers -> LDS buffer `buf`: K
-  // row-major with the chunk index XOR-swizzled by key, V transposed (4 keys of one
-  // dim per 8 bytes) in 16-byte units of two key groups swizzled by dim; keys 0-63 of
-  // the step go to half 0, keys 64-127 to half 1.
-  //
-  // Per-thread constants.  K chunk i of a thread is key kkey0 + KSTRIDE*i, chunk kch
-  // (KSTRIDE is a multiple of 16, so its row inside the block never changes).  The V
-  // task (vhalf, vkg, vj) loads chunk vj of keys 64*vhalf + 4*vkg + i, i < 4: one
-  // block (offset vblk in the step), rows 4*(vkg%4) + i.
+  // Staging of a 128-key step: K and V rows go from global memory straight into LDS
+  // buffer `buf` (keys 0-63 of the step to half 0, 64-127 to half 1), both row-major
+  // with the 16-byte chunk index XOR-swizzled by key.  One wave's 16-byte loads land at
+  // consecutive LDS addresses (lane L at 16*L), i.e. rows kw0 + L/NCH, slot L%NCH, so
+  // a lane fetches the chunk that the row's swizzle puts in its slot.  Thread tid
+  // handles key kkey0 + KSTRIDE*i (i < KCH) of the step, slot kch; the row's residue
+  // mod NCH and its row inside the block are those of kkey0 for every i (KSTRIDE is a
+  // multiple of 16).  Every load is unconditional: a key past kv_end reads a row of
+  // its block, or of block 0 when its table entry is past the sequence.  Scores of
+  // such keys are masked; their V rows are zeroed after landing (a stale NaN times a
+  // zero weight would still be NaN), by the wave that loaded them, once its loads
+  // have completed.
   constexpr int KSTRIDE = kPThreads / NCH;
-  static_assert(KSTRIDE % kBlock == 0, "K rows must stay fixed across a thread's chunks");
+  static_assert(KSTRIDE % kBlock == 0, "rows must stay fixed across a thread's chunks");
   const uint32_t blk_bytes = (uint32_t)a.num_kv_heads * kBlock * D * 2;
   const int kch = tid % NCH;
   const int kkey0 = tid / NCH;
-  // K goes from global memory straight into LDS: one wave's 16-byte loads land at
-  // consecutive LDS addresses (lane L at 16*L), i.e. rows kw0 + L/NCH, slot L%NCH, so
-  // a lane fetches the chunk that the row's swizzle puts in its slot.  The row's
-  // residue mod NCH is that of kkey0 for every i (KSTRIDE is a multiple of NCH).
   const int kw0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (64 / NCH);
-  const char *kthr = reinterpret_cast<const char *>(kpool) +
-                     (((size_t)kvh * kBlock + kkey0 % kBlock) * D +
-                      (kch ^ (kkey0 % NCH)) * 8) * 2;
-  uint4 vreg[4];
-  const bool vtask = tid < 2 * VTH;
-  const int vhalf = tid / VTH;
-  const int vkg = tid & 15;
-  const int vj = (tid % VTH) >> 4;
-  const int vblk = 4 * vhalf + vkg / 4;
-  // V^T row slot of this task's key group: key groups 8*k2 + 4*h + g (k2, h < 2,
-  // g < 4) pair up as 16-byte unit 4*k2 + g, half h, so each MFMA A fragment (keys
-  // 32*k2 + 4*g + 0..3 and 32*k2 + 16 + 4*g + 0..3) is one 16-byte read.
-  const int vpair = 4 * (vkg / 8) + (vkg % 4);
-  const int vpair_h = (vkg / 4) % 2;
-  const char *vthr = reinterpret_cast<const char *>(vpool) +
-                     (((size_t)kvh * kBlock + 4 * (vkg % 4)) * D + vj * 8) * 2;
+  const size_t thr_off = (((size_t)kvh * kBlock + kkey0 % kBlock) * D +
+                          (kch ^ (kkey0 % NCH)) * 8) * 2;
+  const char *kthr = reinterpret_cast<const char *>(kpool) + thr_off;
+  const char *vthr = reinterpret_cast<const char *>(vpool) + thr_off;
 #define PKV_FETCH(st, buf)                                                               \
   do {                                                                                   \
     const int b0_ = ((st) * (kStepKeys / kBlock)) % kTblCache;                           \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const uint32_t blk_ = (uint32_t)s_tbl[b0_ + (kkey0 + KSTRIDE * i) / kBlock];       \
+      const uint64_t off_ =                                                              \
+          (uint64_t)(uint32_t)s_tbl[b0_ + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;   \
       const int key_ = kw0 + KSTRIDE * i;                                                \
-      load_lds16(kthr + (uint64_t)blk_ * blk_bytes,                                      \
-                 (uint32_t)(uintptr_t)(k_lds + ((buf) * 2 + key_ / kHalfKeys) * K_U4 +     \
-                                       (key_ % kHalfKeys) * NCH));                       \
-    }                                                                                    \
-    if (vtask) {                                                                         \
-      const uint32_t blk_ = (uint32_t)s_tbl[b0_ + vblk];                                 \
-      const char *p_ = vthr + (uint64_t)blk_ * blk_bytes;                                \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
-        vreg[i] = *reinterpret_cast<const uint4 *>(p_ + i * D * 2);                      \
+      const int row_ = ((buf) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH; \
+      load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));                      \
+      load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));                      \
     }                                                                                    \
   } while (0)
-  // Zero what lies past kv_end (only the last step has any).
-#define PKV_MASK_REGS(st)                                                                \
+  // After this wave's loads of step st have completed: zero its V slots past kv_end
+  // (only the last step has any).
+#define PKV_ZERO_TAIL(st, buf)                                                           \
   do {                                                                                   \
     const int k0_ = (st) * kStepKeys;                                                    \
     if (k0_ + kStepKeys > kv_end) {                                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) if (k0_ + kHalfKeys * vhalf +        \
-                                                        4 * vkg + i >= kv_end)           \
-          vreg[i] = uint4{};                                                             \
-    }                                                                                    \
-  } while (0)
-#define PKV_STAGE(buf)                                                                   \
-  do {                                                                                   \
-    if (vtask) {                                                                         \
-      uint2 *vt_ = vt_lds + ((buf) * 2 + vhalf) * V_U2 + vpair_h;                        \
-      const uint32_t w_[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},           \
-                                 {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},           \
-                                 {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},           \
-                                 {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};          \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                    \
-        const int d0 = 8 * vj + 2 * e;                                                   \
-        const int d1 = d0 + 1;                                                           \
-        vt_[d0 * 16 + 2 * (vpair ^ (d0 & 7))] =                                          \
-            uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermLo),                    \
-                  __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermLo)};                   \
-        vt_[d1 * 16 + 2 * (vpair ^ (d1 & 7))] =                                          \
-            uint2{__builtin_amdgcn_perm(w_[1][e], w_[0][e], kPermHi),                    \
-                  __builtin_amdgcn_perm(w_[3][e], w_[2][e], kPermHi)};                   \
+      _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                  \
+        const int key_ = kkey0 + KSTRIDE * i;                                            \
+        if (k0_ + key_ >= kv_end)                                                        \
+          v_lds[((buf) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH + kch] = \
+              uint4{};                                                                   \
       }                                                                                  \
     }                                                                                    \
   } while (0)
@@ -427,10 +409,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   }
   if (st0 < nst) {
     PKV_FETCH(st0, st0 & 1);
-    PKV_MASK_REGS(st0);
-    PKV_STAGE(st0 & 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed in LDS
+    PKV_ZERO_TAIL(st0, st0 & 1);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // K landed in LDS (the loads write it directly)
   __syncthreads();
   // Retire every outstanding load (the query fragments in particular) on all paths
   // here.  Otherwise the wait counters merged at the loop head still see the query
@@ -450,7 +431,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     const int kbase = st * kStepKeys + half * kHalfKeys;
     if (kbase < kv_end) {
       const uint4 *kb = k_lds + (buf * 2 + half) * K_U4;
-      const uint2 *vb = vt_lds + (buf * 2 + half) * V_U2;
+      const uint4 *vb = v_lds + (buf * 2 + half) * K_U4;
       const bool edge = (kbase + kHalfKeys - 1 > pos_first) || (kbase + kHalfKeys > kv_end);
       if (edge)
         tile_update<D, true>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
@@ -459,11 +440,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         tile_update<D, false>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
                               l16, lg);
     }
-    if (st + 1 < nst) {
-      PKV_MASK_REGS(st + 1);
-      PKV_STAGE(buf ^ 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // step st+1's K has landed in LDS
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step st+1 have landed
+    if (st + 1 < nst) PKV_ZERO_TAIL(st + 1, buf ^ 1);
     __syncthreads();  // step st+1 staged; everyone is done reading step st
   }
 
@@ -532,8 +510,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 
 #undef PKV_FILL_TBL
 #undef PKV_FETCH
-#undef PKV_MASK_REGS
-#undef PKV_STAGE
+#undef PKV_ZERO_TAIL
 
 // Log-sum-exp merge of the splits of each tile column: out = sum_s 2^(lse_s - M) o_s /
 // sum_s 2^(lse_s - M), M = max_s lse_s.  Each thread owns four dims of one column
