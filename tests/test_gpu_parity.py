@@ -62,6 +62,17 @@ SMALL = {
                                          num_q_heads=32, num_kv_heads=8, head_dim=64,
                                          num_blocks=200, context_lens=[333, 1200, 65],
                                          query_lens=[200, 1, 65], stale="nan"),
+    # head_dim 64 with groups of 2 and 1 (the other two head-group shapes of the
+    # chunk kernel): a context ending on a 128-key step, chunks from position 0,
+    # ragged last blocks
+    "mixed_bf16_d64_g2": lambda s: _case("mixed_bf16_d64_g2", s, dtype="bf16",
+                                         num_q_heads=16, num_kv_heads=8, head_dim=64,
+                                         num_blocks=160, context_lens=[256, 700, 97, 5],
+                                         query_lens=[129, 1, 97, 5], stale="nan"),
+    "mixed_bf16_d64_g1": lambda s: _case("mixed_bf16_d64_g1", s, dtype="bf16",
+                                         num_q_heads=4, num_kv_heads=4, head_dim=64,
+                                         num_blocks=160, context_lens=[640, 383, 1, 130],
+                                         query_lens=[300, 1, 1, 2], stale="nan"),
     "mixed_bf16_g1": lambda s: _case("mixed_bf16_g1", s, dtype="bf16", num_q_heads=4,
                                      num_kv_heads=4, head_dim=128, num_blocks=120,
                                      context_lens=[290, 500, 17],
