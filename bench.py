@@ -28,7 +28,7 @@ Timing
     read and stored, and its slot indices.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                       [--only-main]
+                       [--only-main] [--only-chunk] [--only-scaling]
 """
 from __future__ import annotations
 
@@ -219,6 +219,76 @@ def time_calls(r: Runner, calls: int, fn=None) -> float:
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / calls
+
+
+class DeviceRunner(Runner):
+    """A Runner over batches built directly on the device (one `sets` entry per copy)."""
+
+    def __init__(self, b, sets):
+        import torch
+        import paged_kv_cache_290_amd as pkv
+
+        self.b, self.pkv, self.torch, self.sets = b, pkv, torch, sets
+        for s in sets:
+            s.out = torch.empty_like(s.q)
+        nbytes = pkv.workspace_size(b.num_seqs, b.total_q, b.num_q_heads, b.num_kv_heads,
+                                    b.head_dim, b.max_context_len, sets[0].q.dtype)
+        self.ws = [torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+                   for _ in sets]
+
+
+def measure_batch_scaling(steps: int, warmup: int) -> dict:
+    """Context for the headline: the same decode shape (Llama-3.2-1B heads, 32q/8kv,
+    d=64, contexts U[128, 2048], bf16) at batches 32, 128 and 512, drawn on the device
+    (torch generator seeded by the batch size; no oracle is involved: these are the
+    kernels the parity tests cover).  A call has fixed costs — the launch, the
+    metadata scan and table walk before the first K/V bytes arrive, the merge launch —
+    that weigh less as the bytes per step grow.  Same protocol as the headline: fused
+    steps in one HIP graph over rotating copies (>= 1 GiB in total)."""
+    import types
+
+    import torch
+
+    hq, hkv, d, mb = 32, 8, 64, 128
+    res = {}
+    for batch in (32, 128, 512):
+        g = torch.Generator().manual_seed(batch)
+        ctx = torch.randint(128, 2049, (batch,), generator=g)
+        nb = max(8192, batch * mb)
+        nblk = (ctx + 15) // 16
+        tbl = torch.randperm(nb, generator=g)[: batch * mb].view(batch, mb).to(torch.int32)
+        tbl[torch.arange(mb).view(1, -1) >= nblk.view(-1, 1)] = -1
+        last = ctx - 1
+        slot = tbl[torch.arange(batch), last // 16].long() * 16 + last % 16
+        b = types.SimpleNamespace(
+            num_seqs=batch, total_q=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+            max_context_len=int(ctx.max()), max_query_len=1, scale=d ** -0.5)
+        kv = int(ctx.sum()) * hkv * d * 2 * 2
+        per = (kv + 2 * batch * hq * d * 2 + int(nblk.sum()) * 4 + 8 * batch + 4 +
+               2 * 2 * batch * hkv * d * 2 + 4 * batch)
+        rot = max(2, min(32, math.ceil(ROTATE_BYTES / per)))
+        sets = []
+        for _ in range(rot):
+            s = types.SimpleNamespace()
+            s.k_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
+            s.v_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
+            s.q = torch.randn(batch, hq, d, device="cuda").to(torch.bfloat16)
+            s.k_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
+            s.v_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
+            s.block_tables = tbl.cuda()
+            s.context_lens = ctx.to(torch.int32).cuda()
+            s.query_start_loc = torch.arange(batch + 1, dtype=torch.int32, device="cuda")
+            s.slot_mapping = slot.to(torch.int32).cuda()
+            sets.append(s)
+        r = DeviceRunner(b, sets)
+        ms = time_graph(r, steps, warmup)
+        gbs = per / (ms * 1e-3) / 1e9
+        res[f"batch_{batch}"] = {"bytes_per_step": per, "rotating_copies": rot,
+                                 "ms_per_step": round(ms, 5), "GBs": round(gbs, 1),
+                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del r, sets
+        torch.cuda.empty_cache()
+    return res
 
 
 def rotation_for(b) -> int:
@@ -697,6 +767,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--only-scaling", action="store_true",
+                    help="only the headline decode shape at batches 32, 128 and 512")
     ap.add_argument("--only-chunk", action="store_true",
                     help="only time the prefill chunk of the mixed step (profiling)")
     ap.add_argument("--only-copy", action="store_true",
@@ -751,6 +823,11 @@ def main() -> int:
     if args.only_swap:
         print(json.dumps({"swap": measure_swap()}))
         return 0
+    if args.only_scaling:
+        print(json.dumps({"decode_batch_scaling": measure_batch_scaling(args.steps,
+                                                                        args.warmup)}))
+        return 0
+
     if args.only_chunk:
         print(json.dumps({"prefill_chunk": measure_chunk(make_config("chunked_prefill_mixed",
                                                                      0), args.steps)}))
@@ -821,6 +898,8 @@ def main() -> int:
             torch.cuda.empty_cache()
             extra[name] = ent
         result["workloads"] = extra
+        log("timing the headline decode shape at larger batches")
+        result["decode_batch_scaling"] = measure_batch_scaling(args.steps, args.warmup)
         log("timing copy-on-write block copies")
         result["block_copy"] = measure_block_copy(args.steps)
         log("timing the planner-driven chunked prefill")
