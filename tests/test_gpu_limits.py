@@ -1,0 +1,54 @@
+"""GPU parity at the item limit of one decode launch.
+
+The decode kernel scans its work items (sequences for bf16, query rows for fp32) in
+LDS, at most 2,048 per launch; larger batches are cut into consecutive launches whose
+items and partial slots must not interfere.  Both cases here exceed the limit and are
+compared element by element with the fp64 oracle, through the plain and the fused
+calls.
+"""
+import numpy as np
+import pytest
+
+import oracle.pagedkv_oracle as O
+from tests.gpu_util import DeviceBatch, out_f64, to_raw, tolerance
+from workloads import make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(b, got, ref, what):
+    tol = tolerance(b, ref)
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert (err <= tol).all(), f"{what}: max err {err.max():.3g}"
+
+
+def test_more_sequences_than_one_launch_holds_bf16():
+    rng = np.random.Generator(np.random.PCG64(21))
+    n = 2100
+    ctx = [int(c) for c in rng.integers(1, 80, n, endpoint=True)]
+    nb = sum((c + 15) // 16 for c in ctx) + 16
+    print(f"[case] {n} bf16 decode sequences", flush=True)
+    b = make_batch(rng, name="many_bf16", dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                   head_dim=64, num_blocks=nb, context_lens=ctx, query_lens=[1] * n,
+                   stale="nan")
+    kp, vp, ref = O.step(b)
+    db = DeviceBatch(b)
+    out = db.step()
+    assert to_raw(db.k_pool).tobytes() == kp.tobytes(), "K pool after write"
+    _check(b, out_f64(out), ref, "two calls")
+    db2 = DeviceBatch(b)
+    _check(b, out_f64(db2.step_fused()), ref, "fused call")
+
+
+def test_more_rows_than_one_launch_holds_f32():
+    rng = np.random.Generator(np.random.PCG64(22))
+    print("[case] 2,101 fp32 query rows", flush=True)
+    b = make_batch(rng, name="many_rows_f32", dtype="f32", num_q_heads=4, num_kv_heads=2,
+                   head_dim=64, num_blocks=200, context_lens=[1600, 700, 50],
+                   query_lens=[1500, 600, 1], stale="nan")
+    kp, vp, ref = O.step(b)
+    db = DeviceBatch(b)
+    out = db.step()
+    assert to_raw(db.v_pool).tobytes() == vp.tobytes(), "V pool after write"
+    _check(b, out_f64(out), ref, "fp32 rows")
