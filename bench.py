@@ -29,6 +29,7 @@ Timing
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                        [--only-main] [--only-chunk] [--only-scaling]
+                       [--only-achievable]
 """
 from __future__ import annotations
 
@@ -288,6 +289,107 @@ def measure_batch_scaling(steps: int, warmup: int) -> dict:
                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del r, sets
         torch.cuda.empty_cache()
+    return res
+
+
+def _time_fn(fn, calls: int) -> float:
+    """Average ms of fn() from HIP events on the current stream, the calls queued
+    behind a spin kernel so that they run back to back."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / calls
+
+
+def measure_achievable(calls: int) -> dict:
+    """Measured ceilings to read the rooflines against (the published peaks stay the
+    `peak` of the roofline objects):
+      * HBM read rate of this library's read-only probe (pkv_read_probe): a contiguous
+        1 GiB stream in 4 KiB tiles (the waves sweeping it side by side); scattered
+        2 KiB tiles (the K or V tile of one (block, kv head) at d=64 bf16), a random
+        permutation of a 1 GiB pool, 512 MiB per call; and the same scattered pattern
+        at the headline decode step's K/V bytes, i.e. a pure-read floor for that step
+        (one launch, no metadata walk).  Consecutive calls read disjoint tile sets, so
+        the 256 MB MALL does not serve them.  The best of grids of 2, 4 and 8
+        workgroups per CU is reported.
+      * bf16 GEMM rate of torch.matmul (hipBLASLt) at 8192^3, a measuring stick only.
+    """
+    import torch
+
+    import paged_kv_cache_290_amd as pkv
+    from workloads import make_config
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator().manual_seed(0)
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    pool.random_(0, 255)
+    sink = torch.empty(8 * cus * 4, dtype=torch.int32, device="cuda")
+    res = {}
+
+    def best(lists, tile_bytes, order=None):
+        """Best rate over the grids; calls cycle through `lists` (disjoint tile sets,
+        together larger than the MALL, so a call does not read what the previous
+        calls left in it)."""
+        nbytes = lists[0].numel() * tile_bytes
+        out = {}
+        for per_cu in (2, 4, 8):
+            grid = per_cu * cus
+            src = [order(t, grid * 4) if order else t for t in lists]
+            k = [0]
+
+            def call():
+                pkv.read_probe(pool, src[k[0] % len(src)], tile_bytes, sink, grid)
+                k[0] += 1
+
+            ms = _time_fn(call, calls)
+            out[per_cu] = nbytes / (ms * 1e-3) / 1e9
+        k = max(out, key=out.get)
+        return {"GBs": round(out[k], 1), "frac_of_peak": round(out[k] / HBM_PEAK_GBS, 4),
+                "bytes": nbytes, "wgs_per_cu": k, "tile_sets": len(lists)}
+
+    def sweep(t, waves):
+        # wave w's contiguous share of the list holds tiles w, w + waves, ...: the
+        # waves read neighbouring tiles at the same time (a sweeping front)
+        n = t.numel() // waves * waves
+        return t[:n].view(-1, waves).t().contiguous().view(-1)
+
+    ntiles = (1 << 30) // 2048
+    seq = torch.arange((1 << 30) // 4096, dtype=torch.int32, device="cuda")
+    res["read_contiguous_1GiB"] = best([seq], 4096, order=sweep)
+    perm = torch.randperm(ntiles, generator=g).to(torch.int32).cuda()
+    half = ntiles // 2
+    res["read_scattered_2KiB_512MiB"] = best([perm[:half], perm[half:]], 2048)
+    b = make_config(MAIN, 0)
+    kv_tiles = int(((b.context_lens.astype("int64") + 15) // 16).sum()) * b.num_kv_heads * 2
+    nsets = ntiles // kv_tiles
+    res["read_scattered_2KiB_headline_step"] = best(
+        [perm[i * kv_tiles:(i + 1) * kv_tiles] for i in range(nsets)], 2048)
+    res["read_scattered_2KiB_headline_step"]["note"] = (
+        "as many 2 KiB tiles as the headline step's K and V tiles, one launch per call")
+    del pool, seq, perm
+    torch.cuda.empty_cache()
+
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = _time_fn(lambda: torch.matmul(x, y), max(5, calls // 4))
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    res["bf16_gemm_8192"] = {"TFLOPs": round(tf, 1),
+                             "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFS, 4),
+                             "via": "torch.matmul (hipBLASLt)"}
+    del x, y
+    torch.cuda.empty_cache()
     return res
 
 
@@ -767,6 +869,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--only-achievable", action="store_true",
+                    help="only the measured HBM read and bf16 GEMM ceilings")
     ap.add_argument("--only-scaling", action="store_true",
                     help="only the headline decode shape at batches 32, 128 and 512")
     ap.add_argument("--only-chunk", action="store_true",
@@ -823,6 +927,10 @@ def main() -> int:
     if args.only_swap:
         print(json.dumps({"swap": measure_swap()}))
         return 0
+    if args.only_achievable:
+        print(json.dumps({"achievable": measure_achievable(args.steps)}))
+        return 0
+
     if args.only_scaling:
         print(json.dumps({"decode_batch_scaling": measure_batch_scaling(args.steps,
                                                                         args.warmup)}))
@@ -900,6 +1008,16 @@ def main() -> int:
         result["workloads"] = extra
         log("timing the headline decode shape at larger batches")
         result["decode_batch_scaling"] = measure_batch_scaling(args.steps, args.warmup)
+        log("measuring achievable HBM read and bf16 GEMM rates")
+        ach = measure_achievable(args.steps)
+        ach["headline_call_vs_scattered_read"] = round(
+            roof["achieved"] / ach["read_scattered_2KiB_512MiB"]["GBs"], 4)
+        ach["headline_call_vs_step_sized_read"] = round(
+            roof["achieved"] / ach["read_scattered_2KiB_headline_step"]["GBs"], 4)
+        if "prefill_chunk" in result:
+            ach["chunk_vs_gemm"] = round(
+                result["prefill_chunk"]["achieved"] / ach["bf16_gemm_8192"]["TFLOPs"], 4)
+        result["achievable"] = ach
         log("timing copy-on-write block copies")
         result["block_copy"] = measure_block_copy(args.steps)
         log("timing the planner-driven chunked prefill")

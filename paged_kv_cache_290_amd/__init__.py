@@ -7,5 +7,5 @@ The shared library is loaded lazily on the first call and must have been built w
 """
 from .ops import (BLOCK_SIZE, BlockAllocator, StepBatch, attention,  # noqa: F401
                   attention_with_write, block_keys, copy_blocks, kv_write, plan_step,
-                  swap_bytes, swap_in, swap_out, validate_metadata, workspace_size)
+                  read_probe, swap_bytes, swap_in, swap_out, validate_metadata, workspace_size)
 from ._lib import PagedKVError  # noqa: F401

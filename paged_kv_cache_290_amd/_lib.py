@@ -59,6 +59,8 @@ SIGNATURES = {
                                          _i32, ctypes.c_int, _vp]),
     "paged_kv_swap_in": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                         _i32, ctypes.c_int, _vp]),
+    "pkv_read_probe": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _i32, _i32, _vp, _i32,
+                                      _vp]),
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),

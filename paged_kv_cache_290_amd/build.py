@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip",
-           "planner.hip", "prefix.hip", "swap.hip")
+           "planner.hip", "prefix.hip", "swap.hip", "probe.hip")
 # Host-only C++ (no device code), compiled by the host compiler.
 HOST_SOURCES = ("sha256_x86.cpp",)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

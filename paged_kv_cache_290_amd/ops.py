@@ -456,3 +456,21 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, copies: torch.Tensor
                                           copies.data_ptr(), copies.shape[0], nb, hkv, d,
                                           bs, _dtype_code(k_pool), _stream_handle(stream))
     _lib.check("paged_kv_copy_blocks", st)
+
+
+def read_probe(base: torch.Tensor, tiles: torch.Tensor, tile_bytes: int, sink: torch.Tensor,
+               grid: int, stream=None) -> None:
+    """Measuring aid (pkv_read_probe): read the `tile_bytes`-byte tiles of `base` named
+    by the int32 device tensor `tiles`; `sink` is a uint8/int32 device buffer of at
+    least grid * 16 bytes (one word per wave)."""
+    dev = base.device
+    for n, t in (("base", base), ("tiles", tiles), ("sink", sink)):
+        _on_gpu(n, t, dev)
+    _require(tiles.dtype == torch.int32 and tiles.dim() == 1 and tiles.is_contiguous(),
+             "tiles must be a contiguous int32 vector")
+    _require(base.is_contiguous(), "base must be contiguous")
+    _require(sink.numel() * sink.element_size() >= grid * 16, "sink too small")
+    st = _lib.load().pkv_read_probe(base.data_ptr(), base.numel() * base.element_size(),
+                                    tiles.data_ptr(), tiles.numel(), tile_bytes,
+                                    sink.data_ptr(), grid, _stream_handle(stream))
+    _lib.check("pkv_read_probe", st)

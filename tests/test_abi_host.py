@@ -141,3 +141,24 @@ def test_validator_rejects_bad_metadata():
     assert validate_metadata(*args[:3], sm, args[4]) == (True, -1)
     bt = b.block_tables.copy(); bt[0, 3:] = 999               # unused entries ignored
     assert validate_metadata(bt, *args[1:]) == (True, -1)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(base=None), _lib.PKV_ERR_INVALID_ARG),
+    (dict(tiles=None), _lib.PKV_ERR_INVALID_ARG),
+    (dict(sink=None), _lib.PKV_ERR_INVALID_ARG),
+    (dict(num_tiles=-1), _lib.PKV_ERR_INVALID_ARG),
+    (dict(grid=0), _lib.PKV_ERR_INVALID_ARG),
+    (dict(tile_bytes=0), _lib.PKV_ERR_INVALID_ARG),
+    (dict(tile_bytes=1000), _lib.PKV_ERR_INVALID_ARG),   # not a multiple of 1 KiB
+    (dict(base_bytes=1024), _lib.PKV_ERR_INVALID_ARG),   # smaller than one tile
+    (dict(num_tiles=0), _lib.PKV_OK),                     # nothing to read, no launch
+])
+def test_read_probe_argument_checks(over, want):
+    args = dict(base=1, base_bytes=1 << 20, tiles=2, num_tiles=4, tile_bytes=2048, sink=3,
+                grid=8)
+    args.update(over)
+    lib = _lib.load()
+    assert lib.pkv_read_probe(args["base"], args["base_bytes"], args["tiles"],
+                              args["num_tiles"], args["tile_bytes"], args["sink"],
+                              args["grid"], None) == want
