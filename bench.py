@@ -201,9 +201,10 @@ def time_graph(r: Runner, steps: int, warmup: int, fn=None) -> float:
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def time_calls(r: Runner, calls: int, fn=None) -> float:
+def time_calls(r: Runner, calls: int, fn=None, dist: dict | None = None) -> float:
     """Average duration (ms) of one call of fn (default r.step), from HIP events
-    recorded on the stream the kernels are launched on."""
+    recorded on the stream the kernels are launched on.  If `dist` is given, it
+    receives the 10th, 50th and 90th percentiles of the per-call durations."""
     torch = r.torch
     fn = fn or r.step
     stream = torch.cuda.current_stream()
@@ -219,7 +220,11 @@ def time_calls(r: Runner, calls: int, fn=None) -> float:
         fn(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / calls
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    if dist is not None:
+        for q in (10, 50, 90):
+            dist[f"p{q}_ms"] = round(ts[min(len(ts) - 1, (len(ts) * q) // 100)], 5)
+    return sum(ts) / calls
 
 
 class DeviceRunner(Runner):
@@ -418,11 +423,25 @@ def cpu_baseline(b, budget_s: float = 10.0) -> dict:
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     per_step = el / reps
     gbs = (attention_bytes(b) + write_bytes(b)) / per_step / 1e9
+    # the same with BLAS limited to one thread (a third of the budget)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            O.step(b)
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= budget_s / 3 or reps1 >= 20:
+                break
+    per1 = el1 / reps1
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{reps} whole steps of {b.name} (seed 0), fp64 NumPy, "
                       f"{per_step * 1e3:.1f} ms per step",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round((attention_bytes(b) + write_bytes(b)) / per1 / 1e9, 4),
+                           "unit": "GB/s", "cores": 1,
+                           "sample": f"{reps1} whole steps, {per1 * 1e3:.1f} ms per step"}}
 
 
 # ---------------------------------------------------------------------------
@@ -949,7 +968,8 @@ def main() -> int:
     log(f"timing {args.steps} graph-captured steps over {rot} rotating copies")
     ms = time_graph(r, args.steps, args.warmup)
     ms_two = time_graph(r, args.steps, args.warmup, fn=r.step_two_calls)
-    call_ms = time_calls(r, args.steps)
+    call_dist = {}
+    call_ms = time_calls(r, args.steps, dist=call_dist)
     abytes, wbytes = attention_bytes(b), write_bytes(b)
     value = (abytes + wbytes) / (ms * 1e-3) / 1e9
     achieved = (abytes + wbytes) / (call_ms * 1e-3) / 1e9
@@ -958,8 +978,17 @@ def main() -> int:
             "traffic": traffic_for(MAIN),
             "kernel": "paged_attention_varlen_with_write: decode_streamk_kernel (with "
                       "the slot write) + merge_kernel, one call",
-            "algorithmic_bytes": abytes + wbytes, "avg_ms": round(call_ms, 5)}
+            "algorithmic_bytes": abytes + wbytes, "avg_ms": round(call_ms, 5),
+            "call_percentiles": call_dist}
     del r
+    torch.cuda.empty_cache()
+    # warm: the same copy every step, so K/V may come from the 256 MB MALL (context)
+    rw = Runner(b, 1)
+    ms_warm = time_graph(rw, args.steps, args.warmup)
+    warm = {"ms_per_step": round(ms_warm, 5),
+            "GBs": round((abytes + wbytes) / (ms_warm * 1e-3) / 1e9, 1),
+            "note": "one copy reused every step (unflushed caches); context only"}
+    del rw
     torch.cuda.empty_cache()
 
     result = {
@@ -972,6 +1001,7 @@ def main() -> int:
                    "pool_blocks": 8192, "seed": 0, "rotating_copies": rot,
                    "timed_region": "HIP graph of the K steps"},
         "roofline": roof,
+        "warm_step": warm,
         "two_call_step": {"ms_per_step": round(ms_two, 5),
                           "GBs": round((abytes + wbytes) / (ms_two * 1e-3) / 1e9, 1),
                           "calls": "paged_kv_write then paged_attention_varlen"},
