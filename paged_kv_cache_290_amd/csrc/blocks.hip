@@ -93,27 +93,40 @@ int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context
 }  // namespace pkv
 
 // ---------------------------------------------------------------------------
-// block copy kernel: each thread moves 16-byte pieces of (pair, pool) regions
+// block copy kernel: a persistent grid walks the work units, each kThreads * U
+// consecutive 16-byte pieces of one (pair, pool) block; every thread has its U loads
+// in flight before it stores, and a wave's accesses are contiguous KiB runs.
 // ---------------------------------------------------------------------------
 
 namespace pkv {
 
+template <int U>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     uint4 *__restrict__ k_pool, uint4 *__restrict__ v_pool, const int32_t *__restrict__ pairs,
-    int num_pairs, int num_blocks, int64_t block_vecs) {
-  const int64_t total = (int64_t)num_pairs * 2 * block_vecs;
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t per_pair = 2 * block_vecs;
-    const int pair = (int)(idx / per_pair);
-    const int64_t rem = idx - (int64_t)pair * per_pair;
-    const bool is_v = rem >= block_vecs;
-    const int64_t piece = is_v ? rem - block_vecs : rem;
+    int num_pairs, int num_blocks, int64_t block_vecs, int chunks_per_block) {
+  const int64_t units = (int64_t)num_pairs * 2 * chunks_per_block;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int chunk = (int)(unit % chunks_per_block);
+    const int pp = (int)(unit / chunks_per_block);  // pair * 2 + pool
+    const int pair = pp >> 1;
     const int src = pairs[2 * pair];
     const int dst = pairs[2 * pair + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-    uint4 *pool = is_v ? v_pool : k_pool;
-    pool[(int64_t)dst * block_vecs + piece] = pool[(int64_t)src * block_vecs + piece];
+    uint4 *pool = (pp & 1) ? v_pool : k_pool;
+    const uint4 *from = pool + (int64_t)src * block_vecs;
+    uint4 *to = pool + (int64_t)dst * block_vecs;
+    const int64_t base = (int64_t)chunk * kThreads * U + threadIdx.x;
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * kThreads;
+      if (i < block_vecs) x[u] = from[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * kThreads;
+      if (i < block_vecs) to[i] = x[u];
+    }
   }
 }
 
@@ -226,7 +239,6 @@ pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copie
   const int64_t block_bytes = (int64_t)num_kv_heads * kBlock * head_dim *
                               (dtype == PKV_F32 ? 4 : 2);
   const int64_t block_vecs = block_bytes / 16;
-  const int64_t total = (int64_t)num_copies * 2 * block_vecs;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -234,11 +246,30 @@ pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copie
     (void)hipGetLastError();
     cus = 256;
   }
-  const int64_t want = (total + kThreads - 1) / kThreads;
-  const int grid = (int)(want < (int64_t)cus * 8 ? want : (int64_t)cus * 8);
-  copy_blocks_kernel<<<dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<uint4 *>(k_pool), static_cast<uint4 *>(v_pool), copies, num_copies,
-      num_blocks, block_vecs);
+  // PKV_COPY_UNROLL (1, 2, 4 or 8) and PKV_COPY_WGS_PER_CU override the defaults.
+  const char *eu = getenv("PKV_COPY_UNROLL");
+  const char *eg = getenv("PKV_COPY_WGS_PER_CU");
+  int unroll = eu ? atoi(eu) : 1;
+  int per_cu = eg ? atoi(eg) : 8;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) unroll = 1;
+  if (per_cu < 1 || per_cu > 32) per_cu = 8;
+  const int64_t per_unit = (int64_t)kThreads * unroll;
+  const int chunks = (int)((block_vecs + per_unit - 1) / per_unit);
+  const int64_t units = (int64_t)num_copies * 2 * chunks;
+  const int grid = (int)std::min<int64_t>(units, (int64_t)cus * per_cu);
+  auto *kp = static_cast<uint4 *>(k_pool);
+  auto *vp = static_cast<uint4 *>(v_pool);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (unroll) {
+    case 1: copy_blocks_kernel<1><<<dim3(grid), dim3(kThreads), 0, st>>>(
+        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
+    case 2: copy_blocks_kernel<2><<<dim3(grid), dim3(kThreads), 0, st>>>(
+        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
+    case 4: copy_blocks_kernel<4><<<dim3(grid), dim3(kThreads), 0, st>>>(
+        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
+    default: copy_blocks_kernel<8><<<dim3(grid), dim3(kThreads), 0, st>>>(
+        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
+  }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
