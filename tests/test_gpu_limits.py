@@ -52,3 +52,31 @@ def test_more_rows_than_one_launch_holds_f32():
     out = db.step()
     assert to_raw(db.v_pool).tobytes() == vp.tobytes(), "V pool after write"
     _check(b, out_f64(out), ref, "fp32 rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_broken_lengths_give_zero_rows(dtype, fused):
+    """Sequences whose query count exceeds their context (a broken precondition; the
+    host validator rejects them) produce zero rows, and the other rows of the batch
+    are unaffected.  The batch is built valid, then two context lengths are lowered
+    on the device: a decode row to 0 keys and a 70-row chunk to 50 keys."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(23))
+    print(f"[case] broken lengths dtype={dtype} fused={fused}", flush=True)
+    b = make_batch(rng, name="broken", dtype=dtype, num_q_heads=8, num_kv_heads=2,
+                   head_dim=64, num_blocks=120, context_lens=[100, 40, 200, 230],
+                   query_lens=[1, 1, 70, 30], stale="nan")
+    kp, vp, ref = O.step(b)
+    db = DeviceBatch(b)
+    db.context_lens.copy_(torch.tensor([100, 0, 50, 230], dtype=torch.int32))
+    out = db.step_fused() if fused else db.step()
+    got = out_f64(out)
+    qsl = b.query_start_loc
+    broken = np.zeros(b.total_q, dtype=bool)
+    broken[qsl[1]:qsl[2]] = True   # decode row with no keys
+    broken[qsl[2]:qsl[3]] = True   # 70 rows over 50 keys
+    assert (got[broken] == 0).all(), "rows of broken sequences must be zero"
+    _check(b, got[~broken], ref[~broken], "valid rows")
+    assert to_raw(db.k_pool).tobytes() == kp.tobytes(), "the slot write is unaffected"
