@@ -1,4 +1,5 @@
-"""GPU parity at the item limit of one decode launch.
+"""GPU parity at the limits: item counts beyond one decode launch, broken lengths, and
+chunking invariance.
 
 The decode kernel scans its work items (sequences for bf16, query rows for fp32) in
 LDS, at most 2,048 per launch; larger batches are cut into consecutive launches whose
@@ -80,3 +81,39 @@ def test_broken_lengths_give_zero_rows(dtype, fused):
     assert (got[broken] == 0).all(), "rows of broken sequences must be zero"
     _check(b, got[~broken], ref[~broken], "valid rows")
     assert to_raw(db.k_pool).tobytes() == kp.tobytes(), "the slot write is unaffected"
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 16, 8, 128), ("bf16", 32, 8, 64),
+                                            ("f32", 8, 2, 64)])
+def test_chunk_and_decode_equal_rows_of_one_shot_prefill(dtype, hq, hkv, d):
+    """Chunking invariance on the GPU: in one batch whose three sequences name the same
+    blocks, the rows of a chunk [450, 700) over 700 keys equal rows 450..699 of a
+    one-shot prefill of [0, 700), and a decode row at position 699 equals the last
+    prefill row (same queries; only the first sequence writes the new K/V).  The three
+    are computed by different tiles, splits and kernels, so they agree to the
+    tolerance, and each matches the oracle."""
+    import dataclasses
+
+    rng = np.random.Generator(np.random.PCG64(24))
+    print(f"[case] chunk invariance dtype={dtype} hq={hq} hkv={hkv} d={d}", flush=True)
+    one = make_batch(rng, name="oneshot", dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                     head_dim=d, num_blocks=80, context_lens=[700], query_lens=[700],
+                     stale="nan")
+    a = 450
+    rows = np.concatenate([np.arange(700), np.arange(a, 700), [699]])
+    pad = lambda x: np.concatenate([x, np.zeros((len(rows) - 700,) + x.shape[1:], x.dtype)])  # noqa
+    b = dataclasses.replace(
+        one, name="chunk_invariance",
+        block_tables=np.repeat(one.block_tables, 3, axis=0),
+        context_lens=np.array([700, 700, 700], dtype=one.context_lens.dtype),
+        query_start_loc=np.array([0, 700, 700 + 700 - a, len(rows)],
+                                 dtype=one.query_start_loc.dtype),
+        q=one.q[rows], k_new=pad(one.k_new), v_new=pad(one.v_new),
+        slot_mapping=np.concatenate([one.slot_mapping,
+                                     -np.ones(len(rows) - 700, one.slot_mapping.dtype)]))
+    kp, vp, ref = O.step(b)
+    got = out_f64(DeviceBatch(b).step())
+    _check(b, got, ref, "against the oracle")
+    tol = tolerance(b, ref[a:700])
+    assert (np.abs(got[700:700 + 700 - a] - got[a:700]) <= tol).all(), "chunk rows"
+    assert (np.abs(got[-1] - got[699]) <= tolerance(b, ref[699])).all(), "decode row"
