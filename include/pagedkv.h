@@ -51,10 +51,20 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2, /* block_size != 16, head_dim not 64/128, bad dtype   */
   PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required         */
   PKV_ERR_LAUNCH = 4,      /* the HIP runtime reported an error at launch        */
-  PKV_ERR_OUT_OF_BLOCKS = 5 /* the block allocator has too few free blocks       */
+  PKV_ERR_OUT_OF_BLOCKS = 5, /* the block allocator has too few free blocks      */
+  /* Range markers, not codes: every int32 value is a valid pkv_status, so callers in
+   * any language may pass any integer (unknown values are reported as such). */
+  PKV_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  PKV_STATUS_RANGE_MAX_ = 2147483647
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  /* Range markers, not types: any int32 is accepted (others give UNSUPPORTED). */
+  PKV_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PKV_DTYPE_RANGE_MAX_ = 2147483647
+} pkv_dtype;
 
 #define PKV_BLOCK_SIZE 16
 
