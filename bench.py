@@ -29,7 +29,7 @@ Timing
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                        [--only-main] [--only-chunk] [--only-scaling]
-                       [--only-achievable]
+                       [--only-achievable] [--only-mixed]
 """
 from __future__ import annotations
 
@@ -888,6 +888,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--only-mixed", action="store_true",
+                    help="only the mixed chunked-prefill step (chunk + 31 decodes)")
     ap.add_argument("--only-achievable", action="store_true",
                     help="only the measured HBM read and bf16 GEMM ceilings")
     ap.add_argument("--only-scaling", action="store_true",
@@ -946,6 +948,18 @@ def main() -> int:
     if args.only_swap:
         print(json.dumps({"swap": measure_swap()}))
         return 0
+    if args.only_mixed:
+        bx = make_config("chunked_prefill_mixed", 0)
+        rx = Runner(bx, rotation_for(bx))
+        msx = time_graph(rx, args.steps, args.warmup)
+        ax = time_calls(rx, args.steps)
+        ab, wb = attention_bytes(bx), write_bytes(bx)
+        print(json.dumps({"chunked_prefill_mixed": {
+            "ms_per_step": round(msx, 5), "call_ms": round(ax, 5),
+            "step_GBs": round((ab + wb) / (msx * 1e-3) / 1e9, 1),
+            "step_TFLOPs": round(chunk_flops(bx) / (msx * 1e-3) / 1e12, 2)}}))
+        return 0
+
     if args.only_achievable:
         print(json.dumps({"achievable": measure_achievable(args.steps)}))
         return 0
