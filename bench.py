@@ -29,7 +29,7 @@ Timing
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                        [--only-main] [--only-chunk] [--only-scaling]
-                       [--only-achievable] [--only-mixed]
+                       [--only-achievable] [--only-mixed] [--only-chunk-sweep]
 """
 from __future__ import annotations
 
@@ -537,6 +537,36 @@ def write_traffic(out_dir: str, workload: str = MAIN) -> dict:
     return res
 
 
+def measure_chunk_sweep(calls: int) -> dict:
+    """Context: the chunk kernel at step budgets of 512, 1,024, 2,048 and 3,500 rows,
+    each the last rows of a 3,500-token prompt (positions 3,500 - q .. 3,499, the
+    earlier ones cached), Qwen3-1.7B heads (16q/8kv, d=128, bf16), one sequence, so
+    only the chunk kernel launches; HIP events per call.  Pools of 1,024 shuffled
+    blocks drawn with the seeded generator (the kernel is MFMA-bound; its K/V traffic
+    is ~30 MB per call)."""
+    import numpy as np
+    import torch
+
+    from workloads import make_batch
+
+    res = {}
+    for q in (512, 1024, 2048, 3500):
+        rng = np.random.Generator(np.random.PCG64(q))
+        b = make_batch(rng, name=f"chunk_{q}", dtype="bf16", num_q_heads=16,
+                       num_kv_heads=8, head_dim=128, num_blocks=1024, context_lens=[3500],
+                       query_lens=[q])
+        r = Runner(b, 4)
+        r.write(0)
+        ms = time_calls(r, calls, fn=r.attend)
+        fl = chunk_flops(b)
+        tfs = fl / (ms * 1e-3) / 1e12
+        res[f"rows_{q}"] = {"avg_ms": round(ms, 5), "TFLOPs": round(tfs, 1),
+                            "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4), "flops": fl}
+        del r
+        torch.cuda.empty_cache()
+    return res
+
+
 def measure_chunk(bx, calls: int) -> dict:
     """The 2,017-row prefill chunk of the mixed step alone (sequence 0 only): the
     attention call launches prefill_mfma_kernel only; HIP events per call."""
@@ -888,6 +918,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--only-chunk-sweep", action="store_true",
+                    help="only the chunk kernel at 512/1,024/2,048/3,500-row budgets")
     ap.add_argument("--only-mixed", action="store_true",
                     help="only the mixed chunked-prefill step (chunk + 31 decodes)")
     ap.add_argument("--only-achievable", action="store_true",
@@ -948,6 +980,10 @@ def main() -> int:
     if args.only_swap:
         print(json.dumps({"swap": measure_swap()}))
         return 0
+    if args.only_chunk_sweep:
+        print(json.dumps({"chunk_budget_sweep": measure_chunk_sweep(args.steps)}))
+        return 0
+
     if args.only_mixed:
         bx = make_config("chunked_prefill_mixed", 0)
         rx = Runner(bx, rotation_for(bx))
@@ -1052,6 +1088,8 @@ def main() -> int:
         result["workloads"] = extra
         log("timing the headline decode shape at larger batches")
         result["decode_batch_scaling"] = measure_batch_scaling(args.steps, args.warmup)
+        log("timing the chunk kernel at several step budgets")
+        result["chunk_budget_sweep"] = measure_chunk_sweep(args.steps)
         log("measuring achievable HBM read and bf16 GEMM rates")
         ach = measure_achievable(args.steps)
         ach["headline_call_vs_scattered_read"] = round(
