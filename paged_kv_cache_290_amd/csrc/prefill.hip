@@ -18,8 +18,9 @@
 // The two halves keep separate online-softmax states (an in-workgroup split of the
 // key range) that are merged through LDS at the end.
 //
-// K is staged in LDS row-major and V transposed (both XOR-swizzled so the MFMA
-// fragment reads are bank-conflict free); the next step's global loads are in flight
+// K and V are staged in LDS row-major (each with its own XOR swizzle of the 16-byte
+// chunks, so that the K fragment reads and the transposing V fragment reads are free
+// of bank conflicts); the next step's global loads are in flight
 // while the current step is computed (double-buffered LDS).  Each wave computes the
 // transposed score tile S^T = K Q^T and the update O^T += V^T P^T with
 // v_mfma_f32_16x16x32_bf16.  Working on transposes lets the score accumulator feed
@@ -83,8 +84,29 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const void *p) {
       (__attribute__((address_space(3))) v4i16_t *)(p));
 }
 
+// Slot of 16-byte chunk c of a K row in LDS: c ^ swz_k(row), of a V row: c ^
+// swz_v(row).  Both depend on the row mod 16 only (every row that one thread stages
+// shares them).  The K fragment read sends 16 consecutive rows, one chunk each, to a
+// quarter-wave; the V^T read sends 8 consecutive rows, two adjacent chunks each, to
+// half a wave.  The functions make the 16 (row, slot) pairs of each such group land on
+// different banks, with 16-lane passes over 32 four-byte banks and with 32-lane passes
+// over 64 banks alike (checked exhaustively for both head sizes).  For d = 128 the K
+// slot is c ^ row (rows are 256 bytes, so each starts at bank 0); the V slot uses
+// 2*row, because the same XOR by row would put rows 2j and 2j+1, whose chunk pairs
+// are the same two slots, on the same banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return ((row >> 1) & 3) | (((row ^ (row >> 3)) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return (row << 1) & 15;
+  else return (row & 2) | (((row ^ (row >> 2)) & 1) << 2);
+}
+
 // One wave's update with a 64-key tile: kb and vb = K and V tiles, each row-major
-// [key][16-byte chunk ^ key%NCH]; kbase = position of the tile's first key.  MASK
+// [key][16-byte chunk slot] (slots as above); kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
 // position or past kv_end).
 template <int D, bool MASK>
@@ -109,7 +131,7 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint4 *vb,
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       const int key = sub * 16 + l16;
-      const bf16x8_t af = as_bf16x8(kb[key * NCH + ((4 * ks + lg) ^ (key % NCH))]);
+      const bf16x8_t af = as_bf16x8(kb[key * NCH + ((4 * ks + lg) ^ swz_k<D>(key))]);
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = mfma16(af, qf[cg][ks], sacc[sub][cg]);
     }
@@ -189,7 +211,7 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint4 *vb,
   const int vj = l16 >> 2;
   const int vq = l16 & 3;
   const int vkey = 4 * lg + vj;
-  const int vsw = (vq >> 1) ^ (vkey % NCH);  // chunk of dims 16*mt + 4q is 2mt + q/2
+  const int vsw = (vq >> 1) ^ swz_v<D>(vkey);  // chunk of dims 16*mt + 4q is 2mt + q/2
   const char *vrow = reinterpret_cast<const char *>(vb) + vkey * (NCH * 16) + (vq & 1) * 8;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -351,12 +373,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 
   // Staging of a 128-key step: K and V rows go from global memory straight into LDS
   // buffer `buf` (keys 0-63 of the step to half 0, 64-127 to half 1), both row-major
-  // with the 16-byte chunk index XOR-swizzled by key.  One wave's 16-byte loads land at
-  // consecutive LDS addresses (lane L at 16*L), i.e. rows kw0 + L/NCH, slot L%NCH, so
-  // a lane fetches the chunk that the row's swizzle puts in its slot.  Thread tid
-  // handles key kkey0 + KSTRIDE*i (i < KCH) of the step, slot kch; the row's residue
-  // mod NCH and its row inside the block are those of kkey0 for every i (KSTRIDE is a
-  // multiple of 16).  Every load is unconditional: a key past kv_end reads a row of
+  // with the 16-byte chunk slots swizzled (swz_k, swz_v).  One wave's 16-byte loads
+  // land at consecutive LDS addresses (lane L at 16*L), i.e. rows kw0 + L/NCH, slot
+  // L%NCH, so a lane fetches the chunk that the row's swizzle puts in its slot.  Thread
+  // tid handles key kkey0 + KSTRIDE*i (i < KCH) of the step, slot kch; the row's
+  // residue mod 16, hence its swizzle, and its row inside the block are those of kkey0
+  // for every i (KSTRIDE is a multiple of 16).  Every load is unconditional: a key past kv_end reads a row of
   // its block, or of block 0 when its table entry is past the sequence.  Scores of
   // such keys are masked; their V rows are zeroed after landing (a stale NaN times a
   // zero weight would still be NaN), by the wave that loaded them, once its loads
@@ -367,10 +389,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int kch = tid % NCH;
   const int kkey0 = tid / NCH;
   const int kw0 = __builtin_amdgcn_readfirstlane(tid >> 6) * (64 / NCH);
-  const size_t thr_off = (((size_t)kvh * kBlock + kkey0 % kBlock) * D +
-                          (kch ^ (kkey0 % NCH)) * 8) * 2;
-  const char *kthr = reinterpret_cast<const char *>(kpool) + thr_off;
-  const char *vthr = reinterpret_cast<const char *>(vpool) + thr_off;
+  const size_t row_off = ((size_t)kvh * kBlock + kkey0 % kBlock) * D * 2;
+  const char *kthr = reinterpret_cast<const char *>(kpool) + row_off +
+                     (kch ^ swz_k<D>(kkey0)) * 16;
+  const char *vthr = reinterpret_cast<const char *>(vpool) + row_off +
+                     (kch ^ swz_v<D>(kkey0)) * 16;
 #define PKV_FETCH(st, buf)                                                               \
   do {                                                                                   \
     const int b0_ = ((st) * (kStepKeys / kBlock)) % kTblCache;                           \
