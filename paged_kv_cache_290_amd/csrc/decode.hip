@@ -757,14 +757,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   if (gw >= p.items * p.groups * HG) return;
   const int hh = gw % HG;
   const int seg = gw / HG;
-  const int first = p.seginfo[2 * seg];
-  const int npieces = p.seginfo[2 * seg + 1];
-  if (npieces == 0) return;
   const int g = seg / p.items;
   const int item = seg - g * p.items;
+  // The output row's lookup does not depend on the piece info; it is made to complete
+  // before the branch on that info (the empty asm uses it), so that both round trips
+  // overlap instead of the lookup following the branch.
   int seq, row, keys;
   bool zero;
   item_row<kF32>(a, p.item_base + item, seq, row, keys, zero);
+  const int first = p.seginfo[2 * seg];
+  const int npieces = p.seginfo[2 * seg + 1];
+  asm volatile("" ::"s"(row));
+  if (npieces == 0) return;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int kvh = g / p.num_head_groups;
   const int h = kvh * group + (g - kvh * p.num_head_groups) * HG + hh;
