@@ -407,6 +407,26 @@ def rotation_for(b) -> int:
 # oracle timing (CPU baseline leg)
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's "Model name"; /proc/cpuinfo if lscpu is
+    missing)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(b, budget_s: float = 10.0) -> dict:
     """The CPU oracle (as is) on the main workload: slot write + paged attention,
     repeated whole steps until about `budget_s` seconds have run."""
@@ -435,7 +455,7 @@ def cpu_baseline(b, budget_s: float = 10.0) -> dict:
                 break
     per1 = el1 / reps1
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{reps} whole steps of {b.name} (seed 0), fp64 NumPy, "
                       f"{per_step * 1e3:.1f} ms per step",
             "host_cpus": os.cpu_count(),

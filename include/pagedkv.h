@@ -32,7 +32,7 @@
  *   - Device-resident metadata (slots, table entries, lengths) are trusted
  *     preconditions.  Kernels never access memory outside the buffers whatever their
  *     values, but results for invalid metadata are unspecified;
- *     pkv_validate_metadata() checks host copies.
+ *     pkv_validate_metadata() and pkv_validate_fused_metadata() check host copies.
  *   - No exception crosses the ABI.
  */
 #ifndef PAGEDKV_H
@@ -368,27 +368,6 @@ pkv_status paged_kv_swap_in(void *k_pool, void *v_pool, const int32_t *blocks, i
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             pkv_dtype dtype, void *stream);
 
-/*
- * pkv_read_probe -- measuring aid, not part of the attention path: a read-only pass
- * over `num_tiles` tiles of `tile_bytes` bytes (a multiple of 1,024), tile i starting
- * at byte tiles[i] * tile_bytes of `base`, to measure the HBM read rate the GPU reaches
- * for an access pattern (contiguous tiles, or the scattered 2-8 KiB K/V tiles of a
- * paged decode step; the serving-engine KV page, section 2, puts a sequence's blocks
- * anywhere in the pool).  Reports nothing itself: time it on `stream`.
- *   base   DEVICE buffer of base_bytes bytes (read only).
- *   tiles  int32 [num_tiles] DEVICE tile indices; values outside
- *          [0, base_bytes / tile_bytes) are clamped into it.
- *   sink   uint32 [grid * 4] DEVICE output: one XOR of the loaded words per wave
- *          (keeps the loads from being dropped; no meaning of its own).
- *   grid   workgroups of 256 threads (4 waves); the tiles are split evenly over the
- *          grid * 4 waves in contiguous shares.
- * Errors: null pointers, num_tiles < 0, grid <= 0, tile_bytes not a positive multiple
- * of 1,024 or base_bytes < tile_bytes -> INVALID_ARG.  Asynchronous on `stream`.
- */
-pkv_status pkv_read_probe(const void *base, int64_t base_bytes, const int32_t *tiles,
-                          int32_t num_tiles, int32_t tile_bytes, uint32_t *sink,
-                          int32_t grid, void *stream);
-
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *pkv_status_string(pkv_status status);
 
@@ -406,6 +385,24 @@ pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *con
                                  const int32_t *slot_mapping, int32_t num_seqs,
                                  int32_t total_q, int32_t num_blocks,
                                  int32_t max_blocks_per_seq, int32_t *bad_index);
+
+/*
+ * pkv_validate_fused_metadata -- the checks of pkv_validate_metadata (slot_mapping
+ * required) plus the extra precondition of paged_attention_varlen_with_write: new row
+ * t, the i-th of sequence s with q rows and c keys, is position p = c - q + i, and
+ * slot_mapping[t] == block_tables[s][p / 16] * 16 + p % 16 (the slot a scheduler that
+ * appends tokens in order gives it; serving-engine KV page, section 2, "blocks and
+ * block table": a block fills before the next one is taken).  HOST copies, no device
+ * access.  On failure returns PKV_ERR_INVALID_ARG with *bad_index = the offending
+ * sequence (base checks) or row (slot checks).  Metadata that fails only the extra
+ * check is still valid for paged_kv_write followed by paged_attention_varlen.
+ */
+pkv_status pkv_validate_fused_metadata(const int32_t *block_tables,
+                                       const int32_t *context_lens,
+                                       const int32_t *query_start_loc,
+                                       const int32_t *slot_mapping, int32_t num_seqs,
+                                       int32_t total_q, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t *bad_index);
 
 #ifdef __cplusplus
 }

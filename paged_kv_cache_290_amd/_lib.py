@@ -19,7 +19,7 @@ PKV_ERR_OUT_OF_BLOCKS = 5
 PKV_F32 = 0
 PKV_BF16 = 1
 
-# Every symbol include/pagedkv.h declares, with (restype, argtypes).
+# Every symbol the headers under include/ declare, with (restype, argtypes).
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "paged_kv_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -64,6 +64,8 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_validate_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_validate_fused_metadata": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                   _i32, ctypes.POINTER(ctypes.c_int32)]),
 }
 
 _lib = None

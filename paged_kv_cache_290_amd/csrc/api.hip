@@ -2,7 +2,6 @@
 // kernel launches on the caller's stream.  The library is stateless: it allocates
 // nothing, frees nothing and never synchronises.
 #include <math.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <unordered_set>
@@ -12,14 +11,6 @@
 namespace pkv {
 
 namespace {
-
-int env_int(const char *name, int fallback) {
-  const char *s = getenv(name);
-  if (!s || !*s) return fallback;
-  char *end = nullptr;
-  const long v = strtol(s, &end, 10);
-  return (end && *end == 0 && v >= 0 && v < (1 << 20)) ? (int)v : fallback;
-}
 
 bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
@@ -57,12 +48,10 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
   p.head_group = pick_head_group(p.group, head_dim, dtype);
   p.num_head_groups = p.group / p.head_group;
   p.items = dtype == PKV_F32 ? total_q : num_seqs;
-  // PKV_DECODE_PREFETCH and PKV_DECODE_WGS_PER_CU override the defaults (tuning).
-  int prefetch = env_int("PKV_DECODE_PREFETCH", 1);
-  p.prefetch = (prefetch == 2) ? 2 : 1;
-  int per_cu = env_int("PKV_DECODE_WGS_PER_CU", 2);
-  per_cu = std::max(1, std::min(8, per_cu));
-  p.grid = device_cus() * per_cu;
+  // One block in flight per wave while another is computed, two workgroups of four
+  // waves per compute unit (measured: deeper rings and more workgroups were slower).
+  p.prefetch = 1;
+  p.grid = device_cus() * 2;
   const int chunk = std::min(p.items, kMaxStreamItems);
   const size_t slots = (size_t)chunk * num_kv_heads * p.num_head_groups +
                        (size_t)p.grid * kWaves;
@@ -300,6 +289,37 @@ pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *con
       const int64_t s = slot_mapping[t];
       if (s < 0) continue;
       if (s >= (int64_t)num_blocks * kBlock || !seen.insert(s).second) return fail(t);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_validate_fused_metadata(const int32_t *block_tables,
+                                       const int32_t *context_lens,
+                                       const int32_t *query_start_loc,
+                                       const int32_t *slot_mapping, int32_t num_seqs,
+                                       int32_t total_q, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t *bad_index) {
+  if (bad_index) *bad_index = -1;
+  if (total_q > 0 && !slot_mapping) return PKV_ERR_INVALID_ARG;
+  const pkv_status st =
+      pkv_validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
+                            num_seqs, total_q, num_blocks, max_blocks_per_seq, bad_index);
+  if (st != PKV_OK) return st;
+  // Row i of sequence s (q rows, c keys) is position c - q + i; its slot must be that
+  // position's table slot.
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q0 = query_start_loc[s];
+    const int q_len = query_start_loc[s + 1] - q0;
+    const int ctx = context_lens[s];
+    const int32_t *row = block_tables + (size_t)s * max_blocks_per_seq;
+    for (int i = 0; i < q_len; ++i) {
+      const int pos = ctx - q_len + i;
+      const int64_t want = (int64_t)row[pos / kBlock] * kBlock + pos % kBlock;
+      if (slot_mapping[q0 + i] != want) {
+        if (bad_index) *bad_index = q0 + i;
+        return PKV_ERR_INVALID_ARG;
+      }
     }
   }
   return PKV_OK;

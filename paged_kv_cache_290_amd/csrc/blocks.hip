@@ -100,33 +100,26 @@ int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context
 
 namespace pkv {
 
-template <int U>
+// Copy-on-write block copies: for pair i = (src, dst), both pools' block dst receives
+// block src (all kv heads and offsets).  One flat index runs over (pool, pair, 16-byte
+// piece) with a grid-stride loop: consecutive threads move consecutive pieces of one
+// block, so each wave reads and writes 1 KiB runs.  A pair naming a block outside the
+// pool is skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     uint4 *__restrict__ k_pool, uint4 *__restrict__ v_pool, const int32_t *__restrict__ pairs,
-    int num_pairs, int num_blocks, int64_t block_vecs, int chunks_per_block) {
-  const int64_t units = (int64_t)num_pairs * 2 * chunks_per_block;
-  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int chunk = (int)(unit % chunks_per_block);
-    const int pp = (int)(unit / chunks_per_block);  // pair * 2 + pool
-    const int pair = pp >> 1;
-    const int src = pairs[2 * pair];
-    const int dst = pairs[2 * pair + 1];
+    int num_pairs, int num_blocks, int64_t block_vecs) {
+  const int64_t per_pool = (int64_t)num_pairs * block_vecs;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < 2 * per_pool;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const bool is_v = idx >= per_pool;
+    const int64_t rem = is_v ? idx - per_pool : idx;
+    const int i = (int)(rem / block_vecs);
+    const int64_t piece = rem - (int64_t)i * block_vecs;
+    const int src = pairs[2 * i];
+    const int dst = pairs[2 * i + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-    uint4 *pool = (pp & 1) ? v_pool : k_pool;
-    const uint4 *from = pool + (int64_t)src * block_vecs;
-    uint4 *to = pool + (int64_t)dst * block_vecs;
-    const int64_t base = (int64_t)chunk * kThreads * U + threadIdx.x;
-    uint4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + (int64_t)u * kThreads;
-      if (i < block_vecs) x[u] = from[i];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = base + (int64_t)u * kThreads;
-      if (i < block_vecs) to[i] = x[u];
-    }
+    uint4 *pool = is_v ? v_pool : k_pool;
+    pool[(int64_t)dst * block_vecs + piece] = pool[(int64_t)src * block_vecs + piece];
   }
 }
 
@@ -246,30 +239,12 @@ pkv_status paged_kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *copie
     (void)hipGetLastError();
     cus = 256;
   }
-  // PKV_COPY_UNROLL (1, 2, 4 or 8) and PKV_COPY_WGS_PER_CU override the defaults.
-  const char *eu = getenv("PKV_COPY_UNROLL");
-  const char *eg = getenv("PKV_COPY_WGS_PER_CU");
-  int unroll = eu ? atoi(eu) : 1;
-  int per_cu = eg ? atoi(eg) : 8;
-  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) unroll = 1;
-  if (per_cu < 1 || per_cu > 32) per_cu = 8;
-  const int64_t per_unit = (int64_t)kThreads * unroll;
-  const int chunks = (int)((block_vecs + per_unit - 1) / per_unit);
-  const int64_t units = (int64_t)num_copies * 2 * chunks;
-  const int grid = (int)std::min<int64_t>(units, (int64_t)cus * per_cu);
-  auto *kp = static_cast<uint4 *>(k_pool);
-  auto *vp = static_cast<uint4 *>(v_pool);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  switch (unroll) {
-    case 1: copy_blocks_kernel<1><<<dim3(grid), dim3(kThreads), 0, st>>>(
-        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
-    case 2: copy_blocks_kernel<2><<<dim3(grid), dim3(kThreads), 0, st>>>(
-        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
-    case 4: copy_blocks_kernel<4><<<dim3(grid), dim3(kThreads), 0, st>>>(
-        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
-    default: copy_blocks_kernel<8><<<dim3(grid), dim3(kThreads), 0, st>>>(
-        kp, vp, copies, num_copies, num_blocks, block_vecs, chunks); break;
-  }
+  // Eight workgroups per compute unit, each thread one 16-byte piece per iteration.
+  const int64_t total = 2 * (int64_t)num_copies * block_vecs;
+  const int grid = (int)std::min<int64_t>((total + kThreads - 1) / kThreads, (int64_t)cus * 8);
+  copy_blocks_kernel<<<dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint4 *>(k_pool), static_cast<uint4 *>(v_pool), copies, num_copies,
+      num_blocks, block_vecs);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -848,11 +848,8 @@ static hipError_t launch_decode_t(const AttnArgs &a, const DecodePlan &pl, hipSt
 
 template <typename T, int D, int HG>
 static hipError_t launch_decode_p(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
-  switch (p.prefetch) {
-    case 1: return launch_decode_t<T, D, HG, 1>(a, p, st);
-    case 2: return launch_decode_t<T, D, HG, 2>(a, p, st);
-    default: return hipErrorInvalidValue;
-  }
+  if (p.prefetch != 1) return hipErrorInvalidValue;
+  return launch_decode_t<T, D, HG, 1>(a, p, st);
 }
 
 template <typename T, int D>

@@ -83,12 +83,14 @@ __device__ __forceinline__ uint4 buffer_load16(buffer_rsrc_t r, int offset) {
   return uint4{x.x, x.y, x.z, x.w};
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  This
-// maps the hardware order to a virtual index so that each XCD receives one contiguous
-// range of virtual work, keeping work items that share data on one L2.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  const int per_xcd = (total + 7) >> 3;
-  return (wg & 7) * per_xcd + (wg >> 3);
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2): XCD x
+// receives workgroups x, x+8, x+16, ...  This maps the hardware index to a virtual one
+// so that each XCD receives one contiguous range of virtual work, keeping work items
+// that share data on one L2.  It is a bijection of [0, grid) for every grid size: XCD
+// x holds grid/8 workgroups, plus one when x < grid%8.
+__device__ __forceinline__ int xcd_remap(int wg, int grid) {
+  const int x = wg & 7;
+  return x * (grid >> 3) + min(x, grid & 7) + (wg >> 3);
 }
 
 // Sequence owning global query row `row`: the last s with qsl[s] <= row.

@@ -82,7 +82,7 @@ struct DecodePlan {
   int group;            // G = num_q_heads / num_kv_heads
   int head_group;       // q heads handled together by one wave (divides G)
   int num_head_groups;  // G / head_group
-  int prefetch;         // blocks in flight per wave while one is computed (1-2)
+  int prefetch;         // blocks in flight per wave while one is computed (1)
   int grid;             // persistent decode workgroups
   size_t ws_o_offset, ws_lse_offset, ws_seginfo_offset, ws_bytes;
   void *workspace;      // set by the caller before launching

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int lg = lane >> 4;
 
   const int total = tile_slots * a.num_kv_heads * num_head_groups * ps.splits;
-  int v = xcd_remap(blockIdx.x, total);
+  int v = xcd_remap(blockIdx.x, gridDim.x);
   if (v >= total) return;
   // The splits of one tile are consecutive workgroups (one XCD, shared K/V in its L2).
   const int split = v % ps.splits;

@@ -74,8 +74,14 @@ void sha256_chunk(uint32_t h[8], const uint8_t *p) {
 void sha256(const uint8_t *msg, size_t len, uint8_t out[32]) {
   uint32_t h[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
                    0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
-  // PKV_SHA256_PORTABLE=1 forces the portable rounds (the tests check both paths).
-  static const bool x86 = pkv::sha256_x86_available() && !getenv("PKV_SHA256_PORTABLE");
+  // The SHA extensions are used when the host CPU has them.  A build with
+  // PKV_SHA256_PORTABLE_ONLY defined always takes the portable rounds (the tests build
+  // such a copy to check that path as well).
+#ifdef PKV_SHA256_PORTABLE_ONLY
+  static const bool x86 = false;
+#else
+  static const bool x86 = pkv::sha256_x86_available();
+#endif
   auto chunks = [&](const uint8_t *p, size_t n) {
     if (x86) {
       pkv::sha256_x86_chunks(h, p, n);

@@ -11,6 +11,7 @@
 // that no load can be dropped.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pagedkv_probe.h"
 
 namespace pkv {
 

@@ -27,6 +27,18 @@ def _stream_handle(stream) -> int:
     return s.cuda_stream
 
 
+def _empty_on(stream, *args, **kw) -> torch.Tensor:
+    """torch.empty allocated on the stream the library's kernels will use.  The
+    caching allocator then hands the memory to no other stream's allocation before
+    that stream's work is done (a temporary made on the current stream and dropped
+    on return could be reused by the current stream while a side-stream kernel still
+    writes it)."""
+    if stream is None:
+        return torch.empty(*args, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*args, **kw)
+
+
 def _require(cond: bool, msg: str) -> None:
     if not cond:
         raise ValueError(msg)
@@ -75,7 +87,8 @@ def attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
 
     `max_context_len` / `max_query_len` are host-side upper bounds of the device
     metadata.  `workspace` (uint8) must hold at least workspace_size(...) bytes; when
-    omitted it is allocated here.
+    omitted it is allocated here, like a default `out`, on `stream` (the current
+    stream if None).
     """
     dev = q.device
     for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
@@ -97,14 +110,14 @@ def attention(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
              query_start_loc.shape == (num_seqs + 1,),
              "query_start_loc must be int32 [num_seqs + 1]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty_on(stream, q.shape, dtype=q.dtype, device=dev)
     else:
         _on_gpu("out", out, dev)
         _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     need = workspace_size(num_seqs, total_q, hq, hkv, d, max_context_len, q.dtype) \
         if num_seqs and total_q else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty_on(stream, max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _on_gpu("workspace", workspace, dev)
     lib = _lib.load()
@@ -156,14 +169,14 @@ def attention_with_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
              query_start_loc.shape == (num_seqs + 1,),
              "query_start_loc must be int32 [num_seqs + 1]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty_on(stream, q.shape, dtype=q.dtype, device=dev)
     else:
         _on_gpu("out", out, dev)
         _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     need = workspace_size(num_seqs, total_q, hq, hkv, d, max_context_len, q.dtype) \
         if num_seqs and total_q else 0
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _empty_on(stream, max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _on_gpu("workspace", workspace, dev)
     lib = _lib.load()
@@ -179,8 +192,10 @@ def attention_with_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
 
 
 def validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
-                      num_blocks: int) -> tuple[bool, int]:
-    """Host-side metadata check on CPU int32 arrays/tensors; (ok, bad_index)."""
+                      num_blocks: int, fused: bool = False) -> tuple[bool, int]:
+    """Host-side metadata check on CPU int32 arrays/tensors; (ok, bad_index).  With
+    fused=True also the extra precondition of attention_with_write (each new row's
+    slot is its position's table slot; pkv_validate_fused_metadata)."""
     import numpy as np
 
     bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
@@ -190,7 +205,9 @@ def validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
         np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int32))
     bad = ctypes.c_int32(-1)
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
-    st = _lib.load().pkv_validate_metadata(
+    fn = _lib.load().pkv_validate_fused_metadata if fused else \
+        _lib.load().pkv_validate_metadata
+    st = fn(
         ptr(bt), ptr(cl), ptr(qsl), ptr(sm), cl.shape[0], int(qsl[-1]) if qsl.size else 0,
         num_blocks, bt.shape[1] if bt.ndim == 2 else 0, ctypes.byref(bad))
     return st == _lib.PKV_OK, bad.value

@@ -12,11 +12,12 @@ from paged_kv_cache_290_amd import _lib
 from paged_kv_cache_290_amd.ops import validate_metadata
 from workloads import make_batch, make_config
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedkv.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read()
+                   for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", text)) - {"defined", "sizeof"})
 
@@ -141,6 +142,36 @@ def test_validator_rejects_bad_metadata():
     assert validate_metadata(*args[:3], sm, args[4]) == (True, -1)
     bt = b.block_tables.copy(); bt[0, 3:] = 999               # unused entries ignored
     assert validate_metadata(bt, *args[1:]) == (True, -1)
+
+
+def test_fused_validator_checks_positional_slots():
+    """pkv_validate_fused_metadata: every generated batch passes (its slots are the
+    positions' table slots); a slot that is valid for the two-call path but is not its
+    row's position slot is rejected with that row's index; the base checks still run."""
+    for name in ("tiny_f32_decode", "llama32_1b_decode", "chunked_prefill_mixed"):
+        b = make_config(name, 0)
+        assert validate_metadata(b.block_tables, b.context_lens, b.query_start_loc,
+                                 b.slot_mapping, b.num_blocks, fused=True) == (True, -1)
+    rng = np.random.Generator(np.random.PCG64(1))
+    b = make_batch(rng, name="vf", dtype="bf16", num_q_heads=2, num_kv_heads=1,
+                   head_dim=64, num_blocks=40, context_lens=[20, 40, 5, 33],
+                   query_lens=[1, 3, 1, 0])
+    args = [b.block_tables, b.context_lens, b.query_start_loc, b.slot_mapping, b.num_blocks]
+    assert validate_metadata(*args, fused=True) == (True, -1)
+    free = sorted(set(range(40)) - set(b.block_tables[b.block_tables >= 0].tolist()))
+    for row in range(4):
+        sm = b.slot_mapping.copy()
+        sm[row] = free[0] * 16 + 3                 # unused slot: fine for two calls
+        assert validate_metadata(*args[:3], sm, args[4]) == (True, -1)
+        assert validate_metadata(*args[:3], sm, args[4], fused=True) == (False, row)
+    sm = b.slot_mapping.copy()
+    sm[1], sm[2] = sm[2], sm[1]                    # two rows of one chunk swapped
+    assert validate_metadata(*args[:3], sm, args[4], fused=True) == (False, 1)
+    sm = b.slot_mapping.copy(); sm[0] = -1         # a skipped row is not positional
+    assert validate_metadata(*args[:3], sm, args[4], fused=True) == (False, 0)
+    cl = b.context_lens.copy(); cl[2] = 0          # base check: q_len > context_len
+    assert validate_metadata(args[0], cl, *args[2:], fused=True) == (False, 2)
+    assert validate_metadata(*args[:3], None, args[4], fused=True) == (False, -1)
 
 
 @pytest.mark.parametrize("over,want", [

@@ -2,6 +2,8 @@
 cache enabled, through the C ABI) against the prefix-caching oracle: the same keys
 byte for byte, and the same blocks, reference counts and eviction choices, id for id,
 over scripted and random request streams (no GPU needed)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -175,22 +177,39 @@ def test_prefix_errors():
         block_keys(list(range(32)), parent=b"short")
 
 
-def test_portable_sha256_path_matches_oracle():
-    """The portable SHA-256 rounds (used where the host CPU lacks the SHA extensions),
-    forced in a fresh process, give the same keys as hashlib."""
+def test_portable_sha256_path_matches_oracle(tmp_path):
+    """The portable SHA-256 rounds (used where the host CPU lacks the SHA extensions)
+    give the same keys as hashlib: a copy of the library built with the portable
+    rounds only is loaded directly and its pkv_block_keys checked."""
+    import ctypes
     import subprocess
-    import sys
-    code = (
-        "import numpy as np, oracle.prefix_oracle as P, paged_kv_cache_290_amd as pkv\n"
-        "rng = np.random.Generator(np.random.PCG64(9))\n"
-        "for n, e in ((0, 0), (16, 0), (200, 3), (333, 40)):\n"
-        "    t = [int(x) for x in rng.integers(0, 2**31 - 1, n)]\n"
-        "    ex = bytes(range(e))\n"
-        "    assert pkv.block_keys(t, ex) == P.block_keys(t, ex), (n, e)\n"
-        "print('ok')\n")
-    import os
-    env = dict(os.environ, PKV_SHA256_PORTABLE="1")
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    res = subprocess.run([sys.executable, "-c", code], env=env, cwd=root,
-                         capture_output=True, text=True, timeout=120)
-    assert res.returncode == 0 and "ok" in res.stdout, res.stderr
+
+    from paged_kv_cache_290_amd import _lib, build as B
+    if not all(os.path.exists(os.path.join(B.BUILD_DIR, s.replace(".hip", ".o")))
+               for s in B.SOURCES):
+        B.build()
+    obj = str(tmp_path / "prefix_portable.o")
+    flags = B.CFLAGS + ["-DPKV_SHA256_PORTABLE_ONLY"]
+    subprocess.run([B.HIPCC, *flags, "-c", os.path.join(B.CSRC, "prefix.hip"), "-o", obj],
+                   check=True, capture_output=True)
+    objs = [obj] + [os.path.join(B.BUILD_DIR, s.replace(".hip", ".o"))
+                    for s in B.SOURCES if s != "prefix.hip"] + \
+        [os.path.join(B.BUILD_DIR, s.replace(".cpp", ".host.o")) for s in B.HOST_SOURCES]
+    so = str(tmp_path / "libpagedkv_portable.so")
+    subprocess.run([B.HIPCC, f"--offload-arch={B.ARCH}", "-shared", "-fPIC", *objs, "-o", so],
+                   check=True, capture_output=True)
+    lib = ctypes.CDLL(so)
+    fn = lib.pkv_block_keys
+    fn.restype, fn.argtypes = _lib.SIGNATURES["pkv_block_keys"]
+    rng = np.random.Generator(np.random.PCG64(9))
+    for n, e in ((0, 0), (16, 0), (200, 3), (333, 40)):
+        t = np.ascontiguousarray(rng.integers(0, 2**31 - 1, n), dtype=np.int32)
+        ex = np.frombuffer(bytes(range(e)), dtype=np.uint8) if e else None
+        nb = n // 16
+        out = np.zeros(max(nb, 1) * 32, dtype=np.uint8)
+        got = ctypes.c_int32(0)
+        st = fn(t.ctypes.data if n else None, n, ex.ctypes.data if e else None, e, None,
+                out.ctypes.data, nb, ctypes.byref(got))
+        assert st == 0 and got.value == nb
+        keys = [out.tobytes()[32 * i:32 * i + 32] for i in range(nb)]
+        assert keys == P.block_keys([int(x) for x in t], bytes(range(e))), (n, e)
