@@ -164,6 +164,36 @@ pkv_status paged_attention_varlen_with_write(
     pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * paged_attention_varlen_with_write_noalloc -- paged_attention_varlen_with_write for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, result and
+ * precondition as paged_attention_varlen_with_write, without the workspace: the
+ * split-K partials go to a scratch array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB) that
+ * the library keeps on each GPU it runs on for the life of the process.  The call
+ * allocates and frees nothing.
+ *   - A call whose workspace need (paged_attention_workspace_size for its shapes, with
+ *     the chunk part only when max_query_len > 1) exceeds the scratch size returns
+ *     PKV_ERR_WORKSPACE before any launch; use the workspace entry point then.
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap in time on
+ *     one GPU (different streams, or different host threads) race and give undefined
+ *     results; serialise them (one stream) or use the workspace entry point.  Nothing
+ *     in the scratch needs to start at zero, so no call depends on what the previous
+ *     one left there.
+ *   - The scratch's device address is looked up on the first call on each device
+ *     (make that first call outside graph capture); a runtime failure of that lookup
+ *     returns PKV_ERR_LAUNCH.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status paged_attention_varlen_with_write_noalloc(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    pkv_dtype dtype, void *stream);
+
+/*
  * Block bookkeeping (serving-engine KV page, section 2: "blocks and block table" -- a
  * request takes a new 16-token block when its current one fills; "block sharing" --
  * requests sharing a prompt name the same blocks, each block has a reference count,

@@ -33,6 +33,9 @@ SIGNATURES = {
                                                          _i32, _i32, _i32, _i32, _i32,
                                                          _i32, _i32, _f32, ctypes.c_int,
                                                          _vp, _sz, _vp]),
+    "paged_attention_varlen_with_write_noalloc": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+        _i32, _i32, _i32, _i32, _f32, ctypes.c_int, _vp]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
     "pkv_allocator_num_free": (_i32, [_vp]),

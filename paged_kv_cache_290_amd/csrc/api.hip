@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <unordered_set>
 
 #include "pkv_internal.h"
@@ -90,6 +91,19 @@ PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_
   return p;
 }
 
+// Workspace bytes one attention call uses: the decode partials, and after them the
+// split-chunk partials when the batch may hold chunks (bf16 rows of q_len >= 2).
+static size_t required_workspace(int num_seqs, int total_q, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int max_context_len,
+                                 int max_query_len, pkv_dtype dtype) {
+  const DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads,
+                                      head_dim, max_context_len, dtype);
+  if (!(dtype == PKV_BF16 && max_query_len > 1)) return plan.ws_bytes;
+  return plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                      max_context_len, dtype, plan.ws_bytes)
+      .ws_end;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -172,8 +186,8 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
                                 max_context_len, dtype);
   PrefillPlan pplan = plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, dtype, plan.ws_bytes);
-  const bool chunks_planned = dtype == PKV_BF16 && max_query_len > 1;
-  const size_t need = chunks_planned ? pplan.ws_end : plan.ws_bytes;
+  const size_t need = required_workspace(num_seqs, total_q, num_q_heads, num_kv_heads,
+                                         head_dim, max_context_len, max_query_len, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   plan.workspace = workspace;
   pplan.workspace = workspace;
@@ -255,6 +269,79 @@ pkv_status paged_attention_varlen_with_write(
                         max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
                         num_kv_heads, head_dim, block_size, scale, dtype, workspace,
                         workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of the entry point for callers that cannot allocate.  One array per GPU
+// (each device holds its own copy of this file-scope array from the moment the code
+// object is loaded there until the process ends).  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is taken once per device
+// with hipGetSymbolAddress, with that device current, and only that address is ever
+// passed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or null on a runtime error.
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_addr[dev] = ptr;
+  }
+  return g_scratch_addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_varlen_with_write_noalloc(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+    pkv_dtype dtype, void *stream) {
+  if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  // The size check comes first and needs no device; shapes the attention call rejects
+  // are left to its own checks (they need no scratch).
+  const bool shapes_ok = dtype_ok(dtype) && block_size == kBlock && head_dim_ok(head_dim) &&
+                         num_seqs > 0 && total_q > 0 && num_q_heads > 0 &&
+                         num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+                         max_context_len >= 0 && max_query_len >= 0;
+  const size_t need = shapes_ok ? required_workspace(num_seqs, total_q, num_q_heads,
+                                                     num_kv_heads, head_dim, max_context_len,
+                                                     max_query_len, dtype)
+                                : 0;
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (!ws) return PKV_ERR_LAUNCH;
+  }
+  return attention_impl(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                        context_lens, query_start_loc, num_seqs, total_q, num_blocks,
+                        max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
+                        num_kv_heads, head_dim, block_size, scale, dtype, ws,
+                        (size_t)PKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,

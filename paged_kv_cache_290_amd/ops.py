@@ -191,6 +191,51 @@ def attention_with_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
     return out
 
 
+def attention_with_write_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                 k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                 slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                                 context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                                 *, scale: float, max_context_len: int, max_query_len: int,
+                                 out: torch.Tensor, stream=None) -> torch.Tensor:
+    """attention_with_write without a workspace and with a caller-given `out`: nothing
+    is allocated (paged_attention_varlen_with_write_noalloc; the library's per-GPU
+    scratch holds the partials, so calls that overlap in time on one GPU race)."""
+    dev = q.device
+    for n, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool),
+                 ("v_pool", v_pool), ("slot_mapping", slot_mapping),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start_loc", query_start_loc), ("out", out)):
+        _on_gpu(n, t, dev)
+    _require(q.dim() == 3, "q must be [total_q, Hq, D]")
+    total_q, hq, d = q.shape
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    nb, hkv, bs, d2 = k_pool.shape
+    _require(d2 == d, "head_dim of q and pools differ")
+    _require(q.dtype == k_pool.dtype == v_pool.dtype == k_new.dtype == v_new.dtype,
+             "dtype mismatch")
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _require(tuple(k_new.shape) == (total_q, hkv, d) and k_new.shape == v_new.shape,
+             "k_new/v_new must be [total_q, Hkv, D]")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (total_q,),
+             "slot_mapping must be int32 [total_q]")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2,
+             "block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    num_seqs, max_blocks = block_tables.shape
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (num_seqs,),
+             "context_lens must be int32 [num_seqs]")
+    _require(query_start_loc.dtype == torch.int32 and
+             query_start_loc.shape == (num_seqs + 1,),
+             "query_start_loc must be int32 [num_seqs + 1]")
+    st = _lib.load().paged_attention_varlen_with_write_noalloc(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), slot_mapping.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(),
+        num_seqs, total_q, nb, max_blocks, max_context_len, max_query_len, hq, hkv, d, bs,
+        float(scale), _dtype_code(q), _stream_handle(stream))
+    _lib.check("paged_attention_varlen_with_write_noalloc", st)
+    return out
+
+
 def validate_metadata(block_tables, context_lens, query_start_loc, slot_mapping,
                       num_blocks: int, fused: bool = False) -> tuple[bool, int]:
     """Host-side metadata check on CPU int32 arrays/tensors; (ok, bad_index).  With

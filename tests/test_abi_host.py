@@ -144,6 +144,31 @@ def test_validator_rejects_bad_metadata():
     assert validate_metadata(bt, *args[1:]) == (True, -1)
 
 
+def test_noalloc_entry_point_rejects_beyond_its_scratch():
+    """paged_attention_varlen_with_write_noalloc checks its scratch limit before any
+    device call: shapes whose workspace exceeds PKV_NOALLOC_SCRATCH_BYTES (32 MiB) give
+    PKV_ERR_WORKSPACE; bad shapes still give the attention call's own status (null
+    pointers are never touched)."""
+    lib = _lib.load()
+    fn = lib.paged_attention_varlen_with_write_noalloc
+
+    def call(num_seqs, total_q, hq, hkv, d, max_ctx, max_q, dtype=_lib.PKV_BF16, bs=16):
+        return fn(1, 2, 3, 4, 5, 6, 7, 8, 9, 10, num_seqs, total_q, 4096, 4096, max_ctx,
+                  max_q, hq, hkv, d, bs, 0.125, dtype, None)
+
+    ws = lib.paged_attention_workspace_size
+    assert ws(1, 32512, 1, 1, 128, 32512, _lib.PKV_BF16) > (32 << 20)
+    assert call(1, 32512, 1, 1, 128, 32512, 32512) == _lib.PKV_ERR_WORKSPACE
+    assert ws(2048, 2048, 32, 32, 128, 4096, _lib.PKV_F32) > (32 << 20)
+    assert call(2048, 2048, 32, 32, 128, 4096, 1, _lib.PKV_F32) == _lib.PKV_ERR_WORKSPACE
+    assert call(1, 32512, 1, 1, 96, 32512, 32512) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(1, 32512, 1, 1, 128, 32512, 32512, bs=8) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(2, 2, 6, 4, 128, 100, 1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(0, 0, 1, 1, 128, 0, 0) == _lib.PKV_OK        # empty batch: nothing to do
+    assert fn(1, 2, None, 4, 5, 6, 7, 8, 9, 10, 1, 1, 16, 1, 16, 1, 1, 1, 128, 16, 0.1,
+              _lib.PKV_BF16, None) == _lib.PKV_ERR_INVALID_ARG
+
+
 def test_fused_validator_checks_positional_slots():
     """pkv_validate_fused_metadata: every generated batch passes (its slots are the
     positions' table slots); a slot that is valid for the two-call path but is not its

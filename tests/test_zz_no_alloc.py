@@ -1,0 +1,105 @@
+"""The entry point that allocates nothing (paged_attention_varlen_with_write_noalloc),
+called through the C ABI, against the workspace entry point it is a variant of
+(paged_attention_varlen_with_write): the same output and pools bit for bit, on two
+calls in a row with the second on a smaller input (the scratch keeps the first call's
+contents), for a decode-and-chunk mix and for split chunks (whose partials use the
+second part of the scratch).  Also within the oracle's tolerance."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.pagedkv_oracle as O
+import paged_kv_cache_290_amd as pkv
+from paged_kv_cache_290_amd import _lib
+from tests.gpu_util import DeviceBatch, out_f64, to_raw, tolerance
+from workloads import make_batch, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _noalloc(db, out):
+    """Direct C-ABI call of the no-alloc entry point on the current stream."""
+    b = db.b
+    lib = _lib.load()
+    st = lib.paged_attention_varlen_with_write_noalloc(
+        out.data_ptr(), db.q.data_ptr(), db.k_new.data_ptr(), db.v_new.data_ptr(),
+        db.k_pool.data_ptr(), db.v_pool.data_ptr(), db.slot_mapping.data_ptr(),
+        db.block_tables.data_ptr(), db.context_lens.data_ptr(),
+        db.query_start_loc.data_ptr(), b.num_seqs, b.total_q, b.num_blocks,
+        b.max_blocks_per_seq, b.max_context_len, b.max_query_len, b.num_q_heads,
+        b.num_kv_heads, b.head_dim, 16, ctypes.c_float(b.scale),
+        _lib.PKV_BF16 if b.dtype == "bf16" else _lib.PKV_F32,
+        torch.cuda.current_stream().cuda_stream)
+    _lib.check("paged_attention_varlen_with_write_noalloc", st)
+    torch.cuda.synchronize()
+    return out
+
+
+def _small(seed, **kw):
+    return make_batch(np.random.Generator(np.random.PCG64(seed)), name="noalloc", **kw)
+
+
+CASES = {
+    # the chunked-prefill mixed step, then a smaller decode batch
+    "mixed_then_decode": (lambda: make_config("chunked_prefill_mixed", 2),
+                          lambda: make_config("qwen3_1p7b_decode_640", 3)),
+    # a short chunk split over many workgroups (chunk partials in the scratch), then a
+    # smaller split chunk with decode rows
+    "split_then_smaller_split": (
+        lambda: _small(21, dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128,
+                       num_blocks=420, context_lens=[6000], query_lens=[40], stale="nan"),
+        lambda: _small(22, dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=64,
+                       num_blocks=300, context_lens=[2100, 900, 1500],
+                       query_lens=[7, 1, 1], stale="nan")),
+    # fp32 rows (all through the decode kernel), then fewer of them
+    "f32_then_smaller_f32": (
+        lambda: _small(23, dtype="f32", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       num_blocks=200, context_lens=[300, 1520, 16, 9],
+                       query_lens=[40, 1, 16, 0], stale="nan"),
+        lambda: _small(24, dtype="f32", num_q_heads=4, num_kv_heads=1, head_dim=64,
+                       num_blocks=60, context_lens=[100, 33], query_lens=[9, 1],
+                       stale="nan")),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_noalloc_equals_workspace_entry_point(name):
+    for k, make in enumerate(CASES[name]):
+        b = make()
+        print(f"[case] noalloc {name} call {k}: {b.num_seqs} seqs, {b.total_q} rows",
+              flush=True)
+        ref_db = DeviceBatch(b)
+        want = to_raw(ref_db.step_fused())
+        db = DeviceBatch(b)
+        got = _noalloc(db, torch.empty_like(db.q))
+        assert to_raw(got).tobytes() == want.tobytes(), f"call {k}: output differs"
+        assert to_raw(db.k_pool).tobytes() == to_raw(ref_db.k_pool).tobytes()
+        assert to_raw(db.v_pool).tobytes() == to_raw(ref_db.v_pool).tobytes()
+        kp, vp, ref = O.step(b)
+        assert to_raw(db.k_pool).tobytes() == kp.tobytes()
+        g = out_f64(got)
+        assert np.isfinite(g).all()
+        assert (np.abs(g - ref) <= tolerance(b, ref)).all(), f"call {k}: vs oracle"
+
+
+def test_noalloc_rejects_a_call_beyond_its_scratch():
+    """A batch whose partials need more than the scratch holds (a 32,512-row chunk in
+    255 tiles, each split in two): PKV_ERR_WORKSPACE, no launch, the output and the
+    pools left untouched."""
+    print("[case] noalloc too large", flush=True)
+    b = _small(25, dtype="bf16", num_q_heads=1, num_kv_heads=1, head_dim=128,
+               num_blocks=2040, context_lens=[32512], query_lens=[32512])
+    need = pkv.workspace_size(b.num_seqs, b.total_q, 1, 1, 128, b.max_context_len,
+                              torch.bfloat16)
+    assert need > (32 << 20)
+    db = DeviceBatch(b)
+    before = to_raw(db.k_pool).tobytes()
+    out = torch.full_like(db.q, 7.0)
+    with pytest.raises(pkv.PagedKVError) as ei:
+        _noalloc(db, out)
+    assert ei.value.status == _lib.PKV_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    assert to_raw(db.k_pool).tobytes() == before
