@@ -144,6 +144,11 @@ class Runner:
             s.out = torch.empty_like(s.q)
         nbytes = pkv.workspace_size(b.num_seqs, b.total_q, b.num_q_heads, b.num_kv_heads,
                                     b.head_dim, b.max_context_len, base.q.dtype)
+        self.shared = int(b.meta.get("shared_prefix_blocks", 0))
+        if self.shared:
+            nbytes = max(nbytes, pkv.shared_prefix_workspace_size(
+                b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, self.shared,
+                base.q.dtype))
         self.ws = [torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
                    for _ in self.sets]
 
@@ -169,6 +174,18 @@ class Runner:
                                       max_context_len=b.max_context_len,
                                       max_query_len=b.max_query_len, out=s.out,
                                       workspace=self.ws[i % len(self.sets)])
+
+    def cascade(self, i):
+        """The fused step through the shared-prefix entry point (the shared blocks read
+        once for all rows)."""
+        s = self.sets[i % len(self.sets)]
+        b = self.b
+        self.pkv.attention_shared_prefix(s.q, s.k_pool, s.v_pool, s.block_tables,
+                                         s.context_lens, s.query_start_loc,
+                                         shared_blocks=self.shared, scale=b.scale,
+                                         max_context_len=b.max_context_len, k_new=s.k_new,
+                                         v_new=s.v_new, slot_mapping=s.slot_mapping,
+                                         out=s.out, workspace=self.ws[i % len(self.sets)])
 
     def step(self, i):
         self.fused(i)
@@ -587,6 +604,23 @@ def measure_chunk_sweep(calls: int) -> dict:
     return res
 
 
+def measure_cascade(r: Runner, steps: int, warmup: int) -> dict:
+    """The shared-prefix workload through paged_attention_varlen_shared_prefix (slot
+    write + private tails by the decode kernel, the 187 shared blocks once by the chunk
+    kernel, merge): graph-timed step and event-timed call, GB/s on unique bytes."""
+    b = r.b
+    ms = time_graph(r, steps, warmup, fn=r.cascade)
+    call_ms = time_calls(r, steps, fn=r.cascade)
+    nbytes = attention_bytes(b) + write_bytes(b)
+    return {"ms_per_step": round(ms, 5), "call_ms": round(call_ms, 5),
+            "step_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "call_GBs": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+            "call_hbm_frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "calls": "paged_attention_varlen_shared_prefix (decode_streamk_kernel on the "
+                     "private blocks, prefill_mfma_kernel on the shared run, "
+                     "cascade_merge_kernel)"}
+
+
 def measure_chunk(bx, calls: int) -> dict:
     """The 2,017-row prefill chunk of the mixed step alone (sequence 0 only): the
     attention call launches prefill_mfma_kernel only; HIP events per call."""
@@ -946,6 +980,8 @@ def main() -> int:
                     help="only the measured HBM read and bf16 GEMM ceilings")
     ap.add_argument("--only-scaling", action="store_true",
                     help="only the headline decode shape at batches 32, 128 and 512")
+    ap.add_argument("--only-shared", action="store_true",
+                    help="only the shared-prefix workload, plain and cascade (profiling)")
     ap.add_argument("--only-chunk", action="store_true",
                     help="only time the prefill chunk of the mixed step (profiling)")
     ap.add_argument("--only-copy", action="store_true",
@@ -1014,6 +1050,17 @@ def main() -> int:
             "ms_per_step": round(msx, 5), "call_ms": round(ax, 5),
             "step_GBs": round((ab + wb) / (msx * 1e-3) / 1e9, 1),
             "step_TFLOPs": round(chunk_flops(bx) / (msx * 1e-3) / 1e12, 2)}}))
+        return 0
+
+    if args.only_shared:
+        bx = make_config("shared_prefix_decode", 0)
+        rx = Runner(bx, rotation_for(bx))
+        ab, wb = attention_bytes(bx), write_bytes(bx)
+        ax = time_calls(rx, args.steps)
+        print(json.dumps({"shared_prefix_decode": {
+            "plain_call_ms": round(ax, 5),
+            "plain_call_GBs": round((ab + wb) / (ax * 1e-3) / 1e9, 1),
+            "shared_prefix_cascade": measure_cascade(rx, args.steps, args.warmup)}}))
         return 0
 
     if args.only_achievable:
@@ -1095,6 +1142,7 @@ def main() -> int:
             if name == "shared_prefix_decode":
                 lb = attention_bytes(bx, unique=False)
                 ent["call_logical_GBs"] = round((lb + wb) / (ax * 1e-3) / 1e9, 1)
+                ent["shared_prefix_cascade"] = measure_cascade(rx, args.steps, args.warmup)
             if name == "chunked_prefill_mixed":
                 fl = chunk_flops(bx)
                 ent["step_TFLOPs"] = round(fl / (msx * 1e-3) / 1e12, 2)

@@ -164,6 +164,45 @@ pkv_status paged_attention_varlen_with_write(
     pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Shared-prefix attention (cascade).  Serving-engine KV page, section 2, "block
+ * sharing", and section 4 (prefix cache): requests with a common prompt prefix name
+ * the same physical blocks at the start of their tables.  Attention over a row's whole
+ * context is the log-sum-exp combination of attention over those shared blocks and
+ * attention over the row's own blocks, so the shared keys and values can be read once
+ * for every row of the batch instead of once per row.
+ *
+ * paged_attention_varlen_shared_prefix -- paged_attention_varlen (k_new, v_new and
+ * slot_mapping all NULL) or paged_attention_varlen_with_write (all three given, same
+ * positional-slot precondition) for a batch of decode rows whose tables all begin with
+ * the same `shared_blocks` physical blocks.  Same layouts and result.
+ *   shared_blocks  block_tables[s][lb] == block_tables[0][lb] for lb < shared_blocks
+ *                  and every s, and every sequence's cached context covers them:
+ *                  context_lens[s] - q_len_s >= shared_blocks * 16 (so every row sees
+ *                  every shared key, and no new row falls into a shared block);
+ *                  pkv_validate_shared_prefix() checks host copies.  0 = nothing
+ *                  shared: the call is the plain one (its workspace rules apply).
+ *   workspace      at least paged_attention_shared_prefix_workspace_size(...) bytes
+ *                  (contents need no initialisation).
+ * Supported: bf16, one query row per sequence (max_query_len == 1, total_q ==
+ * num_seqs), num_seqs <= 2,048; other shapes give PKV_ERR_UNSUPPORTED before any
+ * launch (use the plain entry points).  Three launches on `stream`: the decode kernel
+ * over each row's own blocks (leaving partial results), the MFMA chunk kernel over the
+ * shared blocks with every row as a column (leaving partial results per key split),
+ * and a merge per (row, query head).
+ */
+size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t shared_blocks, pkv_dtype dtype);
+pkv_status paged_attention_varlen_shared_prefix(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t shared_blocks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * paged_attention_varlen_with_write_noalloc -- paged_attention_varlen_with_write for
  * callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc.  Same arguments, result and
@@ -433,6 +472,20 @@ pkv_status pkv_validate_fused_metadata(const int32_t *block_tables,
                                        const int32_t *slot_mapping, int32_t num_seqs,
                                        int32_t total_q, int32_t num_blocks,
                                        int32_t max_blocks_per_seq, int32_t *bad_index);
+
+/*
+ * pkv_validate_shared_prefix -- the extra precondition of
+ * paged_attention_varlen_shared_prefix on HOST copies: every table row's first
+ * shared_blocks entries equal row 0's, and context_lens[s] - q_len_s >=
+ * shared_blocks * 16.  On failure returns PKV_ERR_INVALID_ARG with *bad_index = the
+ * offending sequence (-1 for bad sizes or null pointers).  The base checks are
+ * pkv_validate_metadata's.
+ */
+pkv_status pkv_validate_shared_prefix(const int32_t *block_tables,
+                                      const int32_t *context_lens,
+                                      const int32_t *query_start_loc, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int32_t shared_blocks,
+                                      int32_t *bad_index);
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,13 @@ SIGNATURES = {
     "paged_attention_varlen_with_write_noalloc": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
         _i32, _i32, _i32, _i32, _f32, ctypes.c_int, _vp]),
+    "paged_attention_shared_prefix_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32,
+                                                           ctypes.c_int]),
+    "paged_attention_varlen_shared_prefix": (ctypes.c_int, [
+        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+        _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _sz, _vp]),
+    "pkv_validate_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32,
+                                                  ctypes.POINTER(ctypes.c_int32)]),
     "pkv_allocator_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (None, [_vp]),
     "pkv_allocator_num_free": (_i32, [_vp]),

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "blocks.hip",
+SOURCES = ("api.hip", "kv_write.hip", "decode.hip", "prefill.hip", "cascade.hip", "blocks.hip",
            "planner.hip", "prefix.hip", "swap.hip", "probe.hip")
 # Host-only C++ (no device code), compiled by the host compiler.
 HOST_SOURCES = ("sha256_x86.cpp",)

@@ -74,9 +74,9 @@ PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_
   p.tile_slots = prefill_tile_slots(total_q, num_seqs, kPrefillCols / p.head_group);
   p.tiles = p.tile_slots * num_kv_heads * p.num_head_groups;
   // Split the key range when the tiles cannot fill the compute units, keeping at
-  // least two 128-key steps per split.
+  // least two of the kernel's key steps per split.
   const int cus = device_cus();
-  const int steps = (max_context_len + 127) / 128;
+  const int steps = (max_context_len + kPrefillStepKeys - 1) / kPrefillStepKeys;
   p.splits = 1;
   if (dtype == PKV_BF16 && p.tiles > 0 && p.tiles < cus && steps >= 4)
     p.splits = std::max(1, std::min((cus + p.tiles - 1) / p.tiles, steps / 2));
@@ -88,6 +88,29 @@ PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_
     p.ws_col_offset = p.ws_lse_offset + align256(parts * sizeof(float));
     p.ws_end = p.ws_col_offset + align256((size_t)p.tiles * kPrefillCols * sizeof(int));
   }
+  return p;
+}
+
+PrefillPlan plan_shared_run(int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                            int shared_keys, size_t ws_offset) {
+  PrefillPlan p{};
+  const int group = num_q_heads / num_kv_heads;
+  p.head_group = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  p.num_head_groups = group / p.head_group;
+  const int bm = kPrefillCols / p.head_group;
+  p.tile_slots = (total_q + bm - 1) / bm;
+  p.tiles = p.tile_slots * num_kv_heads * p.num_head_groups;
+  // Enough key splits to fill the compute units, two key steps or more each (fewer
+  // splits also mean fewer partials to write and merge: one step per split made the
+  // pass 1.1 us shorter and the merge 1.6 us longer on the 187-block workload).
+  const int cus = device_cus();
+  const int steps = (shared_keys + kPrefillStepKeys - 1) / kPrefillStepKeys;
+  p.splits = std::max(1, std::min((cus + p.tiles - 1) / p.tiles, std::max(1, steps / 2)));
+  const size_t parts = (size_t)p.tiles * p.splits * kPrefillCols;
+  p.ws_o_offset = align256(ws_offset);
+  p.ws_lse_offset = p.ws_o_offset + align256(parts * head_dim * sizeof(float));
+  p.ws_col_offset = p.ws_lse_offset + align256(parts * sizeof(float));
+  p.ws_end = p.ws_col_offset + align256((size_t)p.tiles * kPrefillCols * sizeof(int));
   return p;
 }
 
@@ -342,6 +365,116 @@ pkv_status paged_attention_varlen_with_write_noalloc(
                         max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
                         num_kv_heads, head_dim, block_size, scale, dtype, ws,
                         (size_t)PKV_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t shared_blocks, pkv_dtype dtype) {
+  if (num_seqs <= 0 || num_seqs > kMaxStreamItems || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) ||
+      dtype != PKV_BF16 || shared_blocks <= 0)
+    return 0;
+  // Decode partials of the private keys, then the shared run's key splits.
+  const DecodePlan dp = plan_decode(num_seqs, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    0, dtype);
+  return plan_shared_run(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                         shared_blocks * kBlock, dp.ws_bytes)
+      .ws_end;
+}
+
+pkv_status paged_attention_varlen_shared_prefix(
+    void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,
+    void *v_pool, const int32_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+    int32_t total_q, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_context_len, int32_t max_query_len, int32_t shared_blocks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    float scale, pkv_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool with_write = k_new || v_new || slot_mapping;
+  if (with_write && !(k_new && v_new && slot_mapping)) return PKV_ERR_INVALID_ARG;
+  if (shared_blocks < 0 || max_blocks_per_seq < 0 || shared_blocks > max_blocks_per_seq)
+    return PKV_ERR_INVALID_ARG;
+  if (shared_blocks == 0)  // nothing shared: the plain call
+    return attention_impl(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                          context_lens, query_start_loc, num_seqs, total_q, num_blocks,
+                          max_blocks_per_seq, max_context_len, max_query_len, num_q_heads,
+                          num_kv_heads, head_dim, block_size, scale, dtype, workspace,
+                          workspace_bytes, stream);
+  if (!dtype_ok(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || num_blocks <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_context_len < 0 ||
+      max_query_len < 0 || !isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  // Decode rows (one query per sequence) in bf16, one decode launch's worth of rows.
+  if (dtype != PKV_BF16 || max_query_len != 1 || total_q != num_seqs ||
+      num_seqs > kMaxStreamItems)
+    return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens ||
+      !query_start_loc)
+    return PKV_ERR_INVALID_ARG;
+
+  DecodePlan dp = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                              max_context_len, dtype);
+  dp.skip_blocks = shared_blocks;
+  dp.cascade = true;
+  PrefillPlan sp = plan_shared_run(total_q, num_q_heads, num_kv_heads, head_dim,
+                                   shared_blocks * kBlock, dp.ws_bytes);
+  if (!workspace || workspace_bytes < sp.ws_end) return PKV_ERR_WORKSPACE;
+  dp.workspace = workspace;
+  sp.workspace = workspace;
+
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_query_len = max_query_len;
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  if (with_write) {  // the decode kernel stores the new rows (all past the shared run)
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Private keys (each row's own blocks), the shared run once for every row, then the
+  // merge of both parts per row and head.
+  hipError_t e = launch_decode(a, dp, dtype, st);
+  if (e == hipSuccess) e = launch_shared_run(a, sp, shared_blocks * kBlock, st);
+  if (e == hipSuccess) e = launch_cascade_merge(a, dp, sp, st);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+pkv_status pkv_validate_shared_prefix(const int32_t *block_tables, const int32_t *context_lens,
+                                      const int32_t *query_start_loc, int32_t num_seqs,
+                                      int32_t max_blocks_per_seq, int32_t shared_blocks,
+                                      int32_t *bad_index) {
+  if (bad_index) *bad_index = -1;
+  if (num_seqs < 0 || shared_blocks < 0 || shared_blocks > max_blocks_per_seq ||
+      (num_seqs > 0 && (!block_tables || !context_lens || !query_start_loc)))
+    return PKV_ERR_INVALID_ARG;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int q_len = query_start_loc[s + 1] - query_start_loc[s];
+    bool ok = (int64_t)context_lens[s] - q_len >= (int64_t)shared_blocks * kBlock;
+    for (int lb = 0; ok && lb < shared_blocks; ++lb)
+      ok = block_tables[(size_t)s * max_blocks_per_seq + lb] == block_tables[lb];
+    if (!ok) {
+      if (bad_index) *bad_index = s;
+      return PKV_ERR_INVALID_ARG;
+    }
+  }
+  return PKV_OK;
 }
 
 pkv_status pkv_validate_metadata(const int32_t *block_tables, const int32_t *context_lens,

@@ -130,8 +130,8 @@ __device__ __forceinline__ bool item_row(const AttnArgs &a, int item, int &seq, 
 // workgroup; ends with a barrier.
 template <bool kRows>
 __device__ __forceinline__ void scan_items(const AttnArgs &a, int base, int items,
-                                           int *s_pref, int *s_keys, int *s_row, int *s_seq,
-                                           int *s_tmp) {
+                                           int skip_blocks, int *s_pref, int *s_keys,
+                                           int *s_row, int *s_seq, int *s_tmp) {
   const int tid = threadIdx.x;
   const int per = (items + kThreads - 1) / kThreads;
   const int i0 = min(items, tid * per);
@@ -144,7 +144,7 @@ __device__ __forceinline__ void scan_items(const AttnArgs &a, int base, int item
     s_keys[i] = keys;
     s_row[i] = row;
     s_seq[i] = seq;
-    const int n = (keys + kBlock - 1) / kBlock;
+    const int n = max((keys + kBlock - 1) / kBlock - skip_blocks, 0);
     s_pref[i] = n;
     local += n;
   }
@@ -222,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       static_cast<uint4 *>(const_cast<void *>(a.v_pool))[dst] = vx;
     }
   }
-  scan_items<kF32>(a, p.item_base, p.items, s_pref, s_keys, s_row, s_seq, s_tmp);
+  scan_items<kF32>(a, p.item_base, p.items, p.skip_blocks, s_pref, s_keys, s_row, s_seq,
+                   s_tmp);
   const int rows_total = s_pref[p.items];
   const int64_t T_all = (int64_t)rows_total * p.groups;
   // With fewer blocks than waves only the first T_all waves work.
@@ -275,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
           static_cast<T *>(a.out)[(size_t)row * a.num_q_heads * D + e] = T(0);
     }
     // Per segment (g, item): first partial slot and piece count for the merge kernel
-    // (0 pieces: nothing to merge, the segment was finished in one wave or is empty).
+    // (0 pieces: nothing to merge, the segment was finished in one wave or is empty;
+    // with all_partial a segment finished in one wave is one piece).
     for (int sg = threadIdx.x; sg < p.items * p.groups; sg += kThreads) {
       const int g = sg / p.items;
       const int item = sg - g * p.items;
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
                            kSegCost;  // cost position of the segment's first block
         const int w0 = wave_of_cost(c0);
         const int w1 = wave_of_cost(c0 + (s_pref[item + 1] - s_pref[item]) - 1);
-        if (w1 > w0) {
+        if (w1 > w0 || p.all_partial) {
           first = sg + w0;
           pieces = w1 - w0 + 1;
         }
@@ -438,14 +440,14 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       int lo = m_g == g_first ? it0 : 0;  // last item with s_pref[item] <= r
       while (lo + 1 < p.items && s_pref[lo + 1] <= r) ++lo;
       m_item = lo;
-      m_lb = r - s_pref[lo];
+      m_lb = r - s_pref[lo] + p.skip_blocks;
       m_keys = s_keys[lo];
       const int pb = a.block_tables[(size_t)s_seq[lo] * a.max_blocks_per_seq + m_lb];
       m_ok = pb >= 0 && pb < a.num_blocks;
       m_pb = m_ok ? pb : 0;
     }
     // Pieces start at a segment's first block, and at the wave's first block.
-    uint64_t starts = __builtin_amdgcn_ballot_w64(lane < nc && m_lb == 0);
+    uint64_t starts = __builtin_amdgcn_ballot_w64(lane < nc && m_lb == p.skip_blocks);
     if (c0 == 0) starts |= 1ull;
 
     // Raw buffer loads through a per-tile descriptor.  Prefetches past the chunk (and
@@ -489,14 +491,14 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       if (pc_open) flush();
       const int g = readlane(m_g, i);
       const int item = readlane(m_item, i);
-      const int lb0 = readlane(m_lb, i);
+      const int lb0 = readlane(m_lb, i) - p.skip_blocks;  // first block, counted from the skip
       pc_row = s_row[item];
       pc_keys = s_keys[item];
       pc_h0 = head0(g);
       pc_seg = g * p.items + item;
       const int n_item = s_pref[item + 1] - s_pref[item];
       const int len = min(n_item - lb0, nbw - (c0 + i));
-      pc_whole = lb0 == 0 && len == n_item;
+      pc_whole = !p.all_partial && lb0 == 0 && len == n_item;
       pc_open = true;
       if (qn_block == c0 + i) {
 #pragma unroll
@@ -833,10 +835,13 @@ static hipError_t launch_decode_t(const AttnArgs &a, const DecodePlan &pl, hipSt
     p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(pl.workspace) + pl.ws_lse_offset);
     p.seginfo =
         reinterpret_cast<int *>(static_cast<char *>(pl.workspace) + pl.ws_seginfo_offset);
+    p.skip_blocks = pl.skip_blocks;
+    p.all_partial = pl.cascade ? 1 : 0;
 
     decode_streamk_kernel<T, D, HG, PF><<<dim3(pl.grid), dim3(kThreads), 0, st>>>(a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (pl.cascade) continue;  // one launch (at most kMaxStreamItems rows); merged later
     const int waves = p.items * p.groups * HG;
     merge_kernel<T, D, HG><<<dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, st>>>(
         a, p);

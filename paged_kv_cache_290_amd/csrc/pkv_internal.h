@@ -84,6 +84,9 @@ struct DecodePlan {
   int num_head_groups;  // G / head_group
   int prefetch;         // blocks in flight per wave while one is computed (1)
   int grid;             // persistent decode workgroups
+  int skip_blocks;      // leading blocks of every row left out (a shared prefix), or 0
+  bool cascade;         // every segment leaves a partial; no merge launch (the shared-
+                        // prefix merge combines them with the shared run's partials)
   size_t ws_o_offset, ws_lse_offset, ws_seginfo_offset, ws_bytes;
   void *workspace;      // set by the caller before launching
 };
@@ -119,6 +122,8 @@ struct StreamArgs {
   float *ws_o;           // [slot][head_group][D] normalised partial outputs
   float *ws_lse;         // [slot][head_group] log2-sum-exp of each partial
   int *seginfo;          // [segments][2]: first partial slot, piece count (0: none)
+  int skip_blocks;       // leading logical blocks of every row this launch leaves out
+  int all_partial;       // nonzero: segments finished in one wave also leave a partial
 };
 
 // Launchers (return hipSuccess or the launch error).
@@ -134,6 +139,7 @@ hipError_t launch_decode(const AttnArgs &a, const DecodePlan &p, pkv_dtype dtype
 // one KV head; with fewer tiles than compute units the key range of each tile is split
 // over `splits` workgroups whose partial results a merge kernel combines.
 constexpr int kPrefillCols = 128;
+constexpr int kPrefillStepKeys = 128;  // keys per step of the chunk kernel
 struct PrefillPlan {
   int head_group;       // q heads per tile (4, 2 or 1)
   int num_head_groups;  // G / head_group
@@ -149,13 +155,28 @@ struct PrefillSplit {
   float *o;    // [tile][split][column][D] normalised partial outputs
   float *lse;  // [tile][split][column] log2-sum-exp (-inf: no key seen)
   int *col;    // [tile][column] output row index (row * Hq + head), -1 = unused
+  // Shared-run mode (> 0): every query row of the batch is a column of one chunk over
+  // the first shared_keys keys of table row 0, without a causal limit (each row sees
+  // them all); tile slot t holds rows [t*BM, (t+1)*BM).  Partials are always written.
+  int shared_keys;
 };
 
 PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
                          int head_dim, int max_context_len, pkv_dtype dtype,
                          size_t ws_offset);
+// Plan of the shared-run pass (bf16): tiles of every query row over shared_keys keys,
+// split over enough workgroups to fill the GPU (one or more key steps each).
+PrefillPlan plan_shared_run(int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                            int shared_keys, size_t ws_offset);
 hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &p, pkv_dtype dtype,
                           hipStream_t stream);
+// The shared-run pass (prefill kernel in shared-run mode; partials only).
+hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &p, int shared_keys,
+                             hipStream_t stream);
+// Merge of a shared-prefix batch: per (row, q head), the decode pieces of the private
+// part (plan `dp`, launched with cascade set) and the shared run's splits (plan `sp`).
+hipError_t launch_cascade_merge(const AttnArgs &a, const DecodePlan &dp,
+                                const PrefillPlan &sp, hipStream_t stream);
 
 // Work-slot count of the prefill launch: an upper bound on the number of query tiles
 // over all sequences (each sequence's tiles fit between floor(qsl[s]/BM) + s and the

@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kPThreads = 512;  // 8 waves
 constexpr int kHalfKeys = 64;   // keys per wave group per step
-constexpr int kStepKeys = 128;  // keys per step
+constexpr int kStepKeys = kPrefillStepKeys;  // keys per step (128)
 constexpr int kCols = kPrefillCols;  // columns per workgroup
 constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
@@ -264,30 +264,44 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   v /= ps.splits;
   const int tile = v;
   const int tid = threadIdx.x;
+  const bool shared = ps.shared_keys > 0;  // the shared-run pass of a shared prefix
+  const bool partials = ps.splits > 1 || shared;
   // Split partials: until this tile's columns are known, mark them all unused, so the
   // merge skips tiles that end early (decode rows, empty slots, broken lengths).
-  if (ps.splits > 1 && split == 0 && tid < kCols) ps.col[(size_t)tile * kCols + tid] = -1;
+  if (partials && split == 0 && tid < kCols) ps.col[(size_t)tile * kCols + tid] = -1;
   const int slot = v % tile_slots;
   v /= tile_slots;
   const int hgi = v % num_head_groups;
   const int kvh = v / num_head_groups;
 
-  // Sequence owning this tile slot: the last s with qsl[s]/BMQ + s <= slot.
-  int lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.query_start_loc[mid] / BMQ + mid <= slot) lo = mid; else hi = mid - 1;
+  int seq, q_begin, q_len, qtile, ctx;
+  if (shared) {
+    // Every row of the batch is a column of one chunk over the shared run (table row
+    // 0's first blocks); slot t holds rows [t*BMQ, (t+1)*BMQ).
+    seq = 0;
+    q_begin = 0;
+    q_len = a.total_q;
+    if (slot * BMQ >= q_len) return;
+    qtile = slot;
+    ctx = ps.shared_keys;
+  } else {
+    // Sequence owning this tile slot: the last s with qsl[s]/BMQ + s <= slot.
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.query_start_loc[mid] / BMQ + mid <= slot) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    q_begin = a.query_start_loc[seq];
+    q_len = a.query_start_loc[seq + 1] - q_begin;
+    if (q_len <= 1) return;  // decode rows run in the split-K kernel
+    if (q_begin < 0 || q_begin + q_len > a.total_q) return;
+    const int ntiles = (q_len + BMQ - 1) / BMQ;
+    const int local = slot - (q_begin / BMQ + seq);
+    if (local >= ntiles) return;
+    qtile = ntiles - 1 - local;  // tiles that see the most keys go first
+    ctx = a.context_lens[seq];
   }
-  const int seq = lo;
-  const int q_begin = a.query_start_loc[seq];
-  const int q_len = a.query_start_loc[seq + 1] - q_begin;
-  if (q_len <= 1) return;  // decode rows run in the split-K kernel
-  if (q_begin < 0 || q_begin + q_len > a.total_q) return;
-  const int ntiles = (q_len + BMQ - 1) / BMQ;
-  const int local = slot - (q_begin / BMQ + seq);
-  if (local >= ntiles) return;
-  const int qtile = ntiles - 1 - local;  // tiles that see the most keys go first
-  const int ctx = a.context_lens[seq];
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hbase = kvh * group + hgi * HGP;
   const int qi0 = qtile * BMQ;
@@ -306,10 +320,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     qi = min(qi, nq - 1);  // padding columns repeat a real row; never stored
     col_row[cg] = q_begin + qi0 + qi;
     col_head[cg] = hbase + g;
-    col_pos[cg] = ctx - q_len + qi0 + qi;
+    // A shared run has no causal limit: every row sees all of its keys.
+    col_pos[cg] = shared ? ctx - 1 : ctx - q_len + qi0 + qi;
   }
 
-  if (ctx < q_len) {  // precondition broken: defined as zeros
+  if (!shared && ctx < q_len) {  // precondition broken: defined as zeros
     if (half == 0) {
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg)
@@ -338,7 +353,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     }
   }
 
-  const int pos_first = ctx - q_len + qi0;
+  const int pos_first = shared ? ctx - 1 : ctx - q_len + qi0;
   const int ctx_eff = min(ctx, a.max_blocks_per_seq * kBlock);
   const int kv_end = min(pos_first + nq, ctx_eff);
   const int nst_tile = (kv_end + kStepKeys - 1) / kStepKeys;
@@ -423,7 +438,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 
   PKV_FILL_TBL((st0 * (kStepKeys / kBlock)) / kTblCache * kTblCache);
   __syncthreads();
-  if (ps.splits > 1 && split == 0) {  // after the unused marks: a barrier lies between
+  if (partials && split == 0) {  // after the unused marks: a barrier lies between
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg)
       if (half == 0 && lg == 0 && col_ok[cg])
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     const float L = a0 * lsum[cg] + a1 * l1;
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     if (!col_ok[cg]) continue;
-    if (ps.splits > 1) {
+    if (partials) {
       // This split's normalised output and log2-sum-exp (-inf when it saw no key).
       const size_t pc = ((size_t)tile * ps.splits + split) * kCols + cw * 32 + cg * 16 + l16;
       float *po = ps.o + pc * D;
@@ -575,12 +590,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a, PrefillS
 }
 
 template <int D, int HGP>
-static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, hipStream_t st) {
+static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
+                                   hipStream_t st) {
   const int total = pl.tiles * pl.splits;
   if (total == 0) return hipSuccess;
   PrefillSplit ps{};
   ps.splits = pl.splits;
-  if (pl.splits > 1) {
+  ps.shared_keys = shared_keys;
+  if (pl.splits > 1 || shared_keys > 0) {
     char *w = static_cast<char *>(pl.workspace);
     ps.o = reinterpret_cast<float *>(w + pl.ws_o_offset);
     ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
@@ -590,17 +607,19 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, hip
   prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kPThreads), 0, st>>>(a, pl.num_head_groups,
                                                                        pl.tile_slots, ps);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.splits == 1) return e;
+  // A shared run's partials are merged with the rows' other parts elsewhere.
+  if (e != hipSuccess || pl.splits == 1 || shared_keys > 0) return e;
   prefill_merge_kernel<D><<<dim3(pl.tiles * (kCols * D / 4 / 256)), dim3(256), 0, st>>>(a, ps);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const AttnArgs &a, const PrefillPlan &pl, hipStream_t st) {
+static hipError_t launch_prefill_d(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
+                                   hipStream_t st) {
   switch (pl.head_group) {
-    case 4: return launch_prefill_t<D, 4>(a, pl, st);
-    case 2: return launch_prefill_t<D, 2>(a, pl, st);
-    case 1: return launch_prefill_t<D, 1>(a, pl, st);
+    case 4: return launch_prefill_t<D, 4>(a, pl, shared_keys, st);
+    case 2: return launch_prefill_t<D, 2>(a, pl, shared_keys, st);
+    case 1: return launch_prefill_t<D, 1>(a, pl, shared_keys, st);
   }
   return hipErrorInvalidValue;
 }
@@ -608,8 +627,16 @@ static hipError_t launch_prefill_d(const AttnArgs &a, const PrefillPlan &pl, hip
 hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &pl, pkv_dtype dtype,
                           hipStream_t stream) {
   if (dtype != PKV_BF16) return hipErrorInvalidValue;
-  if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, stream);
-  if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, stream);
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, 0, stream);
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, 0, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
+                             hipStream_t stream) {
+  if (shared_keys <= 0) return hipErrorInvalidValue;
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, shared_keys, stream);
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, shared_keys, stream);
   return hipErrorInvalidValue;
 }
 

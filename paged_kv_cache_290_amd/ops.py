@@ -191,6 +191,96 @@ def attention_with_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
     return out
 
 
+def shared_prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                 head_dim: int, shared_blocks: int,
+                                 dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(_lib.load().paged_attention_shared_prefix_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, shared_blocks, _DTYPES[dtype]))
+
+
+def attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            query_start_loc: torch.Tensor, *, shared_blocks: int,
+                            scale: float, max_context_len: int,
+                            k_new: torch.Tensor | None = None,
+                            v_new: torch.Tensor | None = None,
+                            slot_mapping: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Decode attention for a batch whose tables all start with the same
+    `shared_blocks` blocks (paged_attention_varlen_shared_prefix): the shared keys are
+    read once for all rows.  With k_new/v_new/slot_mapping it is the fused step (their
+    slot write first, as in attention_with_write)."""
+    dev = q.device
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                 ("block_tables", block_tables), ("context_lens", context_lens),
+                 ("query_start_loc", query_start_loc)):
+        _on_gpu(n, t, dev)
+    with_write = k_new is not None
+    _require(with_write == (v_new is not None) == (slot_mapping is not None),
+             "give k_new, v_new and slot_mapping together, or none of them")
+    _require(q.dim() == 3, "q must be [total_q, Hq, D]")
+    total_q, hq, d = q.shape
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pool shape mismatch")
+    nb, hkv, bs, d2 = k_pool.shape
+    _require(d2 == d, "head_dim of q and pools differ")
+    _require(q.dtype == k_pool.dtype == v_pool.dtype, "dtype mismatch")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2,
+             "block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    num_seqs, max_blocks = block_tables.shape
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (num_seqs,),
+             "context_lens must be int32 [num_seqs]")
+    _require(query_start_loc.dtype == torch.int32 and
+             query_start_loc.shape == (num_seqs + 1,),
+             "query_start_loc must be int32 [num_seqs + 1]")
+    if with_write:
+        for n, t in (("k_new", k_new), ("v_new", v_new), ("slot_mapping", slot_mapping)):
+            _on_gpu(n, t, dev)
+        _require(tuple(k_new.shape) == (total_q, hkv, d) and k_new.shape == v_new.shape and
+                 k_new.dtype == v_new.dtype == q.dtype,
+                 "k_new/v_new must be [total_q, Hkv, D] of q's dtype")
+        _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (total_q,),
+                 "slot_mapping must be int32 [total_q]")
+    if out is None:
+        out = _empty_on(stream, q.shape, dtype=q.dtype, device=dev)
+    else:
+        _on_gpu("out", out, dev)
+        _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if workspace is None:
+        need = shared_prefix_workspace_size(num_seqs, hq, hkv, d, shared_blocks, q.dtype) \
+            if shared_blocks > 0 else \
+            (workspace_size(num_seqs, total_q, hq, hkv, d, max_context_len, q.dtype)
+             if num_seqs and total_q else 0)
+        workspace = _empty_on(stream, max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _on_gpu("workspace", workspace, dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    st = _lib.load().paged_attention_varlen_shared_prefix(
+        out.data_ptr(), q.data_ptr(), ptr(k_new), ptr(v_new), k_pool.data_ptr(),
+        v_pool.data_ptr(), ptr(slot_mapping), block_tables.data_ptr(), context_lens.data_ptr(),
+        query_start_loc.data_ptr(), num_seqs, total_q, nb, max_blocks, max_context_len, 1,
+        shared_blocks, hq, hkv, d, bs, float(scale), _dtype_code(q), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _lib.check("paged_attention_varlen_shared_prefix", st)
+    return out
+
+
+def validate_shared_prefix(block_tables, context_lens, query_start_loc,
+                           shared_blocks: int) -> tuple[bool, int]:
+    """Host check of the shared-prefix precondition (pkv_validate_shared_prefix)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    qsl = np.ascontiguousarray(np.asarray(query_start_loc, dtype=np.int32))
+    bad = ctypes.c_int32(-1)
+    st = _lib.load().pkv_validate_shared_prefix(
+        bt.ctypes.data, cl.ctypes.data, qsl.ctypes.data, cl.shape[0],
+        bt.shape[1] if bt.ndim == 2 else 0, shared_blocks, ctypes.byref(bad))
+    return st == _lib.PKV_OK, bad.value
+
+
 def attention_with_write_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                                  k_pool: torch.Tensor, v_pool: torch.Tensor,
                                  slot_mapping: torch.Tensor, block_tables: torch.Tensor,

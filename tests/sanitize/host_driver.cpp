@@ -193,6 +193,36 @@ void validator_and_arguments() {
   EXPECT(paged_attention_workspace_size(32, 32, 32, 8, 64, 2048, PKV_BF16) > 0);
   EXPECT(paged_attention_workspace_size(32, 32, 30, 8, 64, 2048, PKV_BF16) == 0);
   for (int s = -1; s < 8; ++s) EXPECT(pkv_status_string((pkv_status)s) != nullptr);
+  // The fused call's positional slots: row 0 is position 19 (table block 1 = physical
+  // 1, offset 3), row 1 position 29 (table block 1 = physical 3, offset 13).
+  int32_t pos_slots[2] = {1 * 16 + 3, 3 * 16 + 13};
+  EXPECT(pkv_validate_fused_metadata(bt, ctx, qsl, pos_slots, 2, 2, 8, 4, &bad) == PKV_OK);
+  pos_slots[0] = 0 * 16 + 3;
+  EXPECT(pkv_validate_fused_metadata(bt, ctx, qsl, pos_slots, 2, 2, 8, 4, &bad) ==
+         PKV_ERR_INVALID_ARG && bad == 0);
+  pos_slots[0] = 1 * 16 + 3;
+  pos_slots[1] = 2 * 16 + 13;
+  EXPECT(pkv_validate_fused_metadata(bt, ctx, qsl, pos_slots, 2, 2, 8, 4, &bad) ==
+         PKV_ERR_INVALID_ARG && bad == 1);
+  // Shared prefixes: the first table entry differs between the rows.
+  EXPECT(pkv_validate_shared_prefix(bt, ctx, qsl, 2, 4, 1, &bad) == PKV_ERR_INVALID_ARG &&
+         bad == 1);
+  EXPECT(pkv_validate_shared_prefix(bt, ctx, qsl, 2, 4, 0, &bad) == PKV_OK);
+  EXPECT(pkv_validate_shared_prefix(bt, ctx, qsl, 2, 4, 5, &bad) == PKV_ERR_INVALID_ARG);
+  EXPECT(paged_attention_varlen_shared_prefix(p, p, nullptr, nullptr, p, p, nullptr, bt, ctx,
+                                              qsl, 2, 2, 8, 4, 30, 1, 1, 8, 4, 64, 16,
+                                              0.125f, PKV_F32, p, 64, nullptr) ==
+         PKV_ERR_UNSUPPORTED);
+  EXPECT(paged_attention_varlen_shared_prefix(p, p, nullptr, nullptr, p, p, nullptr, bt, ctx,
+                                              qsl, 2, 2, 8, 4, 30, 1, 1, 8, 4, 64, 16,
+                                              0.125f, PKV_BF16, p, 64, nullptr) ==
+         PKV_ERR_WORKSPACE);
+  EXPECT(paged_attention_shared_prefix_workspace_size(2, 8, 4, 64, 1, PKV_BF16) > 64);
+  // The no-alloc call: a batch beyond its scratch is refused before any device call.
+  EXPECT(paged_attention_varlen_with_write_noalloc(p, p, p, p, p, p, slots, bt, ctx, qsl, 1,
+                                                   32512, 8, 4, 32512, 32512, 1, 1, 128, 16,
+                                                   0.125f, PKV_BF16, nullptr) ==
+         PKV_ERR_WORKSPACE);
 }
 
 }  // namespace
