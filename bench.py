@@ -683,13 +683,31 @@ def measure_block_copy(calls: int, pairs: int = 1024) -> dict:
     ms = sum(a.elapsed_time(b) for a, b in evs) / calls
     nbytes = pairs * 2 * (hkv * 16 * d * 2) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    del sets
+    # Context: a plain contiguous device copy of the same bytes (torch's copy_), timed
+    # the same way over four rotating buffer pairs.
+    half = nbytes // 2
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(4)]
+    for a_, b_ in bufs:
+        b_.copy_(a_)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(calls):
+        a_, b_ = bufs[i % 4]
+        evs[i][0].record(stream)
+        b_.copy_(a_)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_plain = sum(a.elapsed_time(b) for a, b in evs) / calls
+    del sets, bufs
     torch.cuda.empty_cache()
     return {"workload": f"{pairs} copy-on-write block copies, 8 kv heads x 16 x 128 bf16 "
                         "blocks, both pools", "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": nbytes, "avg_ms": round(ms, 5),
-            "kernel": "copy_blocks_kernel"}
+            "kernel": "copy_blocks_kernel",
+            "plain_contiguous_copy_GBs": round(nbytes / (ms_plain * 1e-3) / 1e9, 1),
+            "vs_plain_contiguous_copy": round(ms_plain / ms, 4)}
 
 
 

