@@ -147,8 +147,8 @@ class Runner:
         self.shared = int(b.meta.get("shared_prefix_blocks", 0))
         if self.shared:
             nbytes = max(nbytes, pkv.shared_prefix_workspace_size(
-                b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, self.shared,
-                base.q.dtype))
+                b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                self.shared, base.q.dtype))
         self.ws = [torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
                    for _ in self.sets]
 

@@ -184,14 +184,15 @@ pkv_status paged_attention_varlen_with_write(
  *   workspace      at least paged_attention_shared_prefix_workspace_size(...) bytes
  *                  (contents need no initialisation).
  * Supported: bf16, one query row per sequence (max_query_len == 1, total_q ==
- * num_seqs), num_seqs <= 2,048; other shapes give PKV_ERR_UNSUPPORTED before any
- * launch (use the plain entry points).  Three launches on `stream`: the decode kernel
+ * num_seqs); other shapes give PKV_ERR_UNSUPPORTED before any launch (use the plain
+ * entry points).  The workspace query takes the call's max_context_len.  Three launches on `stream`: the decode kernel
  * over each row's own blocks (leaving partial results), the MFMA chunk kernel over the
  * shared blocks with every row as a column (leaving partial results per key split),
  * and a merge per (row, query head).
  */
 size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_context_len,
                                                     int32_t shared_blocks, pkv_dtype dtype);
 pkv_status paged_attention_varlen_shared_prefix(
     void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,

@@ -37,7 +37,7 @@ SIGNATURES = {
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
         _i32, _i32, _i32, _i32, _f32, ctypes.c_int, _vp]),
     "paged_attention_shared_prefix_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32,
-                                                           ctypes.c_int]),
+                                                           _i32, ctypes.c_int]),
     "paged_attention_varlen_shared_prefix": (ctypes.c_int, [
         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
         _i32, _i32, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _sz, _vp]),

@@ -42,25 +42,42 @@ static int device_cus() {
 }
 
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
-                       int head_dim, int max_context_len, pkv_dtype dtype) {
-  (void)max_context_len;
+                       int head_dim, int max_context_len, pkv_dtype dtype, int skip_blocks,
+                       bool cascade) {
   DecodePlan p{};
   p.group = num_q_heads / num_kv_heads;
   p.head_group = pick_head_group(p.group, head_dim, dtype);
   p.num_head_groups = p.group / p.head_group;
   p.items = dtype == PKV_F32 ? total_q : num_seqs;
-  // One block in flight per wave while another is computed, two workgroups of four
-  // waves per compute unit (measured: deeper rings and more workgroups were slower).
-  p.prefetch = 1;
-  p.grid = device_cus() * 2;
-  const int chunk = std::min(p.items, kMaxStreamItems);
-  const size_t slots = (size_t)chunk * num_kv_heads * p.num_head_groups +
-                       (size_t)p.grid * kWaves;
+  p.skip_blocks = skip_blocks;
+  p.cascade = cascade;
+  // Workgroup size: bf16 waves hold 128 registers (four per SIMD), so a compute unit
+  // runs one 16-wave or two 8-wave workgroups.  16 waves per segment while the
+  // segments fit the compute units one each; 8 once they do not (two per unit, and the
+  // hardware spreads further rounds of workgroups as units free up).  fp32 rows: 8
+  // waves of 256 registers, one workgroup per unit.
+  const int64_t segments = (int64_t)p.items * num_kv_heads * p.num_head_groups;
+  const int64_t cus = device_cus();
+  p.waves = (dtype == PKV_BF16 && segments <= cus) ? kDecodeWavesMax : kDecodeWavesMin;
+  // Key ranges per segment: one, unless a wave would take more than kBlocksPerWave
+  // blocks of the longest row, or the segments alone leave compute units idle (then
+  // as many as fill them, each range keeping a block per wave or more).
+  const int64_t nb = std::max<int64_t>(
+      (max_context_len + kBlock - 1) / kBlock - (int64_t)skip_blocks, 1);
+  const int64_t cap = (int64_t)p.waves * kBlocksPerWave;
+  int64_t splits = (nb + cap - 1) / cap;
+  if (segments > 0 && segments * splits < cus) {
+    const int64_t fill = (cus + segments - 1) / segments;
+    const int64_t keep = (nb + p.waves - 1) / p.waves;  // ranges with >= 1 block per wave
+    splits = std::max(splits, std::min(fill, keep));
+  }
+  p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, 1 << 16));
+  const bool partials = p.splits > 1 || cascade;
+  const size_t parts = (size_t)segments * p.splits * p.head_group;
   p.ws_o_offset = 0;
-  p.ws_lse_offset = align256(slots * p.head_group * head_dim * sizeof(float));
-  p.ws_seginfo_offset = p.ws_lse_offset + align256(slots * p.head_group * sizeof(float));
-  const size_t segments = (size_t)chunk * num_kv_heads * p.num_head_groups;
-  p.ws_bytes = p.items > 0 ? p.ws_seginfo_offset + align256(segments * 2 * sizeof(int)) : 0;
+  p.ws_lse_offset = align256(parts * head_dim * sizeof(float));
+  p.ws_bytes = (p.items > 0 && partials) ? p.ws_lse_offset + align256(parts * sizeof(float))
+                                         : 0;
   return p;
 }
 
@@ -369,14 +386,15 @@ pkv_status paged_attention_varlen_with_write_noalloc(
 
 size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_context_len,
                                                     int32_t shared_blocks, pkv_dtype dtype) {
-  if (num_seqs <= 0 || num_seqs > kMaxStreamItems || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) ||
-      dtype != PKV_BF16 || shared_blocks <= 0)
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || dtype != PKV_BF16 ||
+      shared_blocks <= 0 || max_context_len < 0)
     return 0;
   // Decode partials of the private keys, then the shared run's key splits.
   const DecodePlan dp = plan_decode(num_seqs, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                    0, dtype);
+                                    max_context_len, dtype, shared_blocks, true);
   return plan_shared_run(num_seqs, num_q_heads, num_kv_heads, head_dim,
                          shared_blocks * kBlock, dp.ws_bytes)
       .ws_end;
@@ -407,18 +425,15 @@ pkv_status paged_attention_varlen_shared_prefix(
       max_query_len < 0 || !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
-  // Decode rows (one query per sequence) in bf16, one decode launch's worth of rows.
-  if (dtype != PKV_BF16 || max_query_len != 1 || total_q != num_seqs ||
-      num_seqs > kMaxStreamItems)
+  // Decode rows (one query per sequence) in bf16.
+  if (dtype != PKV_BF16 || max_query_len != 1 || total_q != num_seqs)
     return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens ||
       !query_start_loc)
     return PKV_ERR_INVALID_ARG;
 
   DecodePlan dp = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                              max_context_len, dtype);
-  dp.skip_blocks = shared_blocks;
-  dp.cascade = true;
+                              max_context_len, dtype, shared_blocks, true);
   PrefillPlan sp = plan_shared_run(total_q, num_q_heads, num_kv_heads, head_dim,
                                    shared_blocks * kBlock, dp.ws_bytes);
   if (!workspace || workspace_bytes < sp.ws_end) return PKV_ERR_WORKSPACE;

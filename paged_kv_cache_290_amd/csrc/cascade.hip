@@ -20,11 +20,11 @@ namespace pkv {
 namespace {
 
 struct CascadeArgs {
-  // decode pieces of the private keys
-  const float *dec_o;    // [slot][dec_hg][D]
-  const float *dec_lse;  // [slot][dec_hg]
-  const int *seginfo;    // [segment][2]: first slot, piece count
+  // key ranges of the private keys (the decode kernel's partials)
+  const float *dec_o;    // [segment][range][dec_hg][D]
+  const float *dec_lse;  // [segment][range][dec_hg]
   int dec_hg, dec_nhg;   // query heads per decode segment, segments per kv head
+  int dec_splits;        // ranges per segment
   // shared-run splits
   const float *sh_o;     // [tile][split][column][D]
   const float *sh_lse;   // [tile][split][column]
@@ -47,11 +47,9 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(AttnArgs a, Cas
   const int group = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / group;
   const int w = h - kvh * group;
-  // Private pieces: segment (decode head group, item), piece i in slot first + i.  The
-  // piece info does not depend on the row lookup: both loads are issued together.
+  // Private ranges: segment (decode head group, item), range i at slot dbase + i*hg.
   const int seg = (kvh * c.dec_nhg + w / c.dec_hg) * a.num_seqs + item;
-  const int first = c.seginfo[2 * seg];
-  const int npieces = c.seginfo[2 * seg + 1];
+  const int npieces = c.dec_splits;
   const int row = a.query_start_loc[item];
   const int q_len = a.query_start_loc[item + 1] - row;
   const int ctx = a.context_lens[item];
@@ -62,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(AttnArgs a, Cas
     for (int e = 0; e < DW; ++e) out[lane + 64 * e] = T(0);
     return;
   }
-  const size_t dbase = (size_t)first * c.dec_hg + (w % c.dec_hg);
+  const size_t dbase = (size_t)seg * c.dec_splits * c.dec_hg + (w % c.dec_hg);
   // Shared splits: the row is column (w % sh_hg) * bm + row % bm of tile slot row / bm.
   const int bm = kPrefillCols / c.sh_hg;
   const int tile = (kvh * c.sh_nhg + w / c.sh_hg) * c.sh_tile_slots + row / bm;
@@ -129,9 +127,9 @@ hipError_t launch_cascade_merge(const AttnArgs &a, const DecodePlan &dp, const P
   char *dw = static_cast<char *>(dp.workspace);
   c.dec_o = reinterpret_cast<const float *>(dw + dp.ws_o_offset);
   c.dec_lse = reinterpret_cast<const float *>(dw + dp.ws_lse_offset);
-  c.seginfo = reinterpret_cast<const int *>(dw + dp.ws_seginfo_offset);
   c.dec_hg = dp.head_group;
   c.dec_nhg = dp.num_head_groups;
+  c.dec_splits = dp.splits;
   char *sw = static_cast<char *>(sp.workspace);
   c.sh_o = reinterpret_cast<const float *>(sw + sp.ws_o_offset);
   c.sh_lse = reinterpret_cast<const float *>(sw + sp.ws_lse_offset);

@@ -1,5 +1,7 @@
-// Decode attention over the paged KV pool: balanced split-K (stream-K) over the
-// context, then a log-sum-exp merge.
+// Decode attention over the paged KV pool: one workgroup per (row, kv-head group)
+// segment, its waves taking the segment's blocks in turn and merging their states in
+// LDS; long segments are cut into a few key ranges whose partial results a merge
+// kernel combines.
 //
 // Method (pages cited by title and section):
 //  * Inference-engine page (xiaohu-jiedu), prefill/decode section: a decode step has
@@ -9,20 +11,19 @@
 //    16-token blocks anywhere in the pool; the kernel follows the request's block
 //    table and must give the same result as a contiguous cache.
 //
-// Work decomposition.  A segment is (kv-head group g, row): the blocks one row must
-// read for the HG query heads of group g.  All segments, concatenated in (g, row,
-// block) order, form one sequence of T blocks.  The grid is persistent (a fixed
-// number of workgroups per CU) and wave w of the W waves takes the contiguous range
-// [w*T/W, (w+1)*T/W), so every wave streams the same number of blocks whatever the
-// context lengths.  A segment that lies inside one wave is finished there; a segment
-// cut across waves leaves one normalised partial (o, log2-sum-exp) per piece, in
-// workspace slot (segment + wave), and the merge kernel combines them.  Slots of
-// different segments never collide: segment s+1 starts at or after the last wave of
-// segment s, so its slots start past segment s's.
+// Work decomposition.  A segment is (row, kv-head group g): the blocks one row reads
+// for the HG query heads of group g.  Its blocks are cut into `splits` contiguous
+// ranges (one unless a wave would get more than kBlocksPerWave blocks, or the
+// segments alone cannot fill the GPU), one workgroup of NW waves per range; wave w
+// takes blocks w, w+NW, w+2NW, ... of the range, so the waves of a workgroup stream
+// within one block of each other whatever the segment's length.  The waves' online-
+// softmax states meet in LDS at the end: with one range the workgroup writes the
+// output itself (no scan over the batch, no second launch); with several each range
+// leaves a normalised partial (o, log2-sum-exp) for the merge kernel.
 //
 // Per block a wave reads one contiguous (block, kv head) tile of K and of V (2-8 KB
 // each) with 16-byte-per-lane raw buffer loads and uses it for all HG query heads
-// (grouped-query reuse), keeping PF blocks in flight in a register ring while it
+// (grouped-query reuse), keeping the next block in flight in a register ring while it
 // computes one.  Softmax runs in log2 units (scores times scale*log2 e, exp2).  Every
 // lane keeps running sums for its own tokens, all scaled by one wave-uniform reference
 // max per head; the reference is raised only when some score exceeds it by more than
@@ -34,11 +35,6 @@
 #include "pkv_internal.h"
 
 namespace pkv {
-
-// Set-up cost of a segment (query load, flush of a partial) for the static split of the
-// work, in K/V bytes streamed in the same time: measured best at 4-6 blocks of 4 KiB
-// (d=64 bf16) and ~2 blocks of 8 KiB (d=128 bf16).
-constexpr int kSegCostBytes = 20 * 1024;
 
 constexpr float kRescaleSlack = 8.0f;
 
@@ -125,89 +121,45 @@ __device__ __forceinline__ bool item_row(const AttnArgs &a, int item, int &seq, 
   return true;
 }
 
-// Per-item block counts -> exclusive prefix in LDS (s_pref[0..items], s_pref[items] =
-// total), visible keys in s_keys, query row and sequence in s_row / s_seq.  Whole
-// workgroup; ends with a barrier.
-template <bool kRows>
-__device__ __forceinline__ void scan_items(const AttnArgs &a, int base, int items,
-                                           int skip_blocks, int *s_pref, int *s_keys,
-                                           int *s_row, int *s_seq, int *s_tmp) {
-  const int tid = threadIdx.x;
-  const int per = (items + kThreads - 1) / kThreads;
-  const int i0 = min(items, tid * per);
-  const int i1 = min(items, i0 + per);
-  int local = 0;
-  for (int i = i0; i < i1; ++i) {
-    int seq = 0, row = 0, keys;
-    bool zero;
-    if (!item_row<kRows>(a, base + i, seq, row, keys, zero)) keys = 0;
-    s_keys[i] = keys;
-    s_row[i] = row;
-    s_seq[i] = seq;
-    const int n = max((keys + kBlock - 1) / kBlock - skip_blocks, 0);
-    s_pref[i] = n;
-    local += n;
-  }
-  s_tmp[tid] = local;
-  __syncthreads();
-  if (tid < 64) {  // exclusive scan of the 256 thread totals by one wave
-    int v0 = s_tmp[4 * tid], v1 = s_tmp[4 * tid + 1], v2 = s_tmp[4 * tid + 2],
-        v3 = s_tmp[4 * tid + 3];
-    const int sum = v0 + v1 + v2 + v3;
-    int incl = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (tid >= d) incl += o;
-    }
-    int ex = incl - sum;
-    s_tmp[4 * tid] = ex; ex += v0;
-    s_tmp[4 * tid + 1] = ex; ex += v1;
-    s_tmp[4 * tid + 2] = ex; ex += v2;
-    s_tmp[4 * tid + 3] = ex; ex += v3;
-    if (tid == 63) s_pref[items] = ex;
-  }
-  __syncthreads();
-  int run = s_tmp[tid];
-  for (int i = i0; i < i1; ++i) {
-    const int n = s_pref[i];
-    s_pref[i] = run;
-    run += n;
-  }
-  __syncthreads();
+
+// Waves per SIMD the decode kernel is compiled for: bf16 rows four (128 registers
+// each: one 16-wave workgroup or two 8-wave workgroups per compute unit), fp32 rows two
+// (their wider tiles need more registers per wave).
+template <typename T>
+constexpr int decode_waves_per_simd() {
+  return std::is_same<T, float>::value ? 2 : 4;
 }
 
-template <typename T, int D, int HG, int PF>
-__global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, StreamArgs p) {
+template <typename T, int D, int HG, int NW>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<T>(), decode_waves_per_simd<T>())))
+void decode_kernel(AttnArgs a, SegArgs p) {
   constexpr bool kF32 = std::is_same<T, float>::value;
   using M = DecodeMap<T, D>;
   constexpr int CPR = M::CPR, TPI = M::TPI, NV = M::NV, EPC = M::EPC, WPC = M::WPC;
   constexpr int kTileBytes = kBlock * D * (int)sizeof(T);
-  // Segment set-up cost in blocks (one block = a K tile and a V tile).
-  constexpr int kSegCost =
-      kSegCostBytes / (2 * kTileBytes) > 1 ? kSegCostBytes / (2 * kTileBytes) : 1;
+  constexpr int PF = 1;  // blocks in flight per wave while one is computed
 
-  __shared__ int s_pref[kMaxStreamItems + 1];
-  __shared__ int s_keys[kMaxStreamItems];
-  __shared__ int s_row[kMaxStreamItems];
-  __shared__ int s_seq[kMaxStreamItems];
-  __shared__ int s_tmp[kThreads];
   // bf16 path: per wave and ring slot, partial scores [j*HG + hh][lane] and the bf16
   // weights [token group][head][j] exchanged between the lanes of the wave.
   constexpr int kRed = kF32 ? 1 : NV * HG * 64;
   constexpr int kPw = kF32 ? 1 : 16 * HG / 2;
-  __shared__ float s_red[kWaves][PF + 1][kRed];
-  __shared__ uint32_t s_pw[kWaves][PF + 1][kPw];
+  __shared__ float s_red[NW][PF + 1][kRed];
+  __shared__ uint32_t s_pw[NW][PF + 1][kPw];
+  // The waves' states for the merge: unnormalised outputs, reference max, weight sum.
+  __shared__ float s_o[NW][HG][D];
+  __shared__ float s_ml[NW][HG][2];
 
-  if (a.k_new != nullptr && p.item_base == 0) {
-    // Fused slot write of every new row (16-byte pieces spread over the grid); its
-    // latency overlaps the item scan.  Nothing in this launch reads those slots.
+  if (a.k_new != nullptr) {
+    // Fused slot write of every new row (16-byte pieces spread over the grid).  No
+    // workgroup reads those slots from the pool: each decode row's newest key and
+    // value come from k_new / v_new below, and chunk rows run in a later launch.
     constexpr int kRowVecs = D * (int)sizeof(T) / 16;
     const int64_t total = (int64_t)a.total_q * a.num_kv_heads * kRowVecs;
     const int64_t per_token = (int64_t)a.num_kv_heads * kRowVecs;
     const int64_t num_slots = (int64_t)a.num_blocks * kBlock;
-    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * kThreads) {
+    for (int64_t idx = (int64_t)blockIdx.x * (64 * NW) + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * (64 * NW)) {
       const int64_t t = idx / per_token;
       const int rem = (int)(idx - t * per_token);
       const int h = rem / kRowVecs;
@@ -222,101 +174,55 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       static_cast<uint4 *>(const_cast<void *>(a.v_pool))[dst] = vx;
     }
   }
-  scan_items<kF32>(a, p.item_base, p.items, p.skip_blocks, s_pref, s_keys, s_row, s_seq,
-                   s_tmp);
-  const int rows_total = s_pref[p.items];
-  const int64_t T_all = (int64_t)rows_total * p.groups;
-  // With fewer blocks than waves only the first T_all waves work.
-  const int W = (int)min<int64_t>((int64_t)gridDim.x * kWaves, T_all);
-  // The static split balances cost, not blocks: each segment costs its blocks plus
-  // kSegCost block-equivalents of set-up (query load, a partial's flush), so a wave
-  // whose range crosses segment starts gets fewer blocks.  In cost order a segment
-  // (g, item) starts at g*rows_cost + s_pref[item] + kSegCost*item, and its block lb
-  // sits at that start + kSegCost + lb.  Wave w owns the cost range
-  // [w*T_cost/W, (w+1)*T_cost/W); its blocks stay one contiguous run in block order.
-  const int64_t rows_cost = (int64_t)rows_total + (int64_t)kSegCost * p.items;
-  const int64_t T_cost = rows_cost * p.groups;
-  // Every product and quotient below fits in 31 bits for all but huge batches; then
-  // the divisions run in 32-bit arithmetic (64-bit division is a long instruction
-  // sequence on the GPU, and these sit on the path to the first block).
-  const bool narrow = T_cost * (int64_t)(W + 1) < (int64_t)INT32_MAX;
-  auto quot = [narrow](int64_t x, int64_t y) -> int64_t {
-    return narrow ? (int64_t)((uint32_t)x / (uint32_t)y) : x / y;
-  };
-  auto wave_of_cost = [&](int64_t c) { return (int)quot((c + 1) * W - 1, T_cost); };
-  // Blocks (in block order) whose cost position is below c (c wave-uniform).  The
-  // item holding c is found with one LDS read and a ballot when there are at most 64
-  // items (lane i tests item i), else by binary search.
-  auto blocks_before = [&](int64_t c) -> int64_t {
-    const int64_t g = quot(c, rows_cost);
-    const int64_t cc = c - g * rows_cost;
-    int lo;  // last item whose cost start is <= cc (item 0 starts at 0)
-    if (p.items <= 64) {
-      const int ln = threadIdx.x & 63;
-      const bool le = ln < p.items && s_pref[ln] + (int64_t)kSegCost * ln <= cc;
-      lo = 63 - __builtin_clzll(__builtin_amdgcn_ballot_w64(le));
-    } else {
-      lo = 0;
-      int hi = p.items - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] + (int64_t)kSegCost * mid <= cc) lo = mid; else hi = mid - 1;
-      }
-    }
-    const int64_t off = cc - (s_pref[lo] + (int64_t)kSegCost * lo);
-    return g * rows_total + s_pref[lo] + (off > kSegCost ? off - kSegCost : 0);
-  };
-  if (blockIdx.x == 0) {
+
+  // Segment and range of this workgroup (uniform over the workgroup, so every early
+  // return below is taken by all its waves).  Virtual order (g, item, split): the
+  // workgroups of one kv-head group sit on one XCD, sharing its L2 for shared blocks.
+  const int64_t total_wg = (int64_t)p.items * p.groups * p.splits;
+  int64_t v = xcd_remap(blockIdx.x, gridDim.x);
+  if (v >= total_wg) return;
+  const int split = (int)(v % p.splits);
+  v /= p.splits;
+  const int item = (int)(v % p.items);
+  const int g = (int)(v / p.items);
+  const int seg = g * p.items + item;
+  int seq, row, keys;
+  bool zero;
+  if (!item_row<kF32>(a, item, seq, row, keys, zero)) return;  // not a decode row
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int kvh = g / p.num_head_groups;
+  const int h0 = kvh * group + (g - kvh * p.num_head_groups) * HG;
+  const size_t part = ((size_t)seg * p.splits + split) * HG;  // partial slot of head 0
+  if (zero) {
     // Rows of sequences that break q_len <= context_len: defined as zeros.
-    for (int i = threadIdx.x; i < p.items; i += kThreads) {
-      int seq, row, keys;
-      bool zero;
-      if (item_row<kF32>(a, p.item_base + i, seq, row, keys, zero) && zero)
-        for (int e = 0; e < a.num_q_heads * D; ++e)
-          static_cast<T *>(a.out)[(size_t)row * a.num_q_heads * D + e] = T(0);
-    }
-    // Per segment (g, item): first partial slot and piece count for the merge kernel
-    // (0 pieces: nothing to merge, the segment was finished in one wave or is empty;
-    // with all_partial a segment finished in one wave is one piece).
-    for (int sg = threadIdx.x; sg < p.items * p.groups; sg += kThreads) {
-      const int g = sg / p.items;
-      const int item = sg - g * p.items;
-      int first = 0, pieces = 0;
-      if (s_pref[item + 1] > s_pref[item]) {
-        const int64_t c0 = (int64_t)g * rows_cost + s_pref[item] + (int64_t)kSegCost * item +
-                           kSegCost;  // cost position of the segment's first block
-        const int w0 = wave_of_cost(c0);
-        const int w1 = wave_of_cost(c0 + (s_pref[item + 1] - s_pref[item]) - 1);
-        if (w1 > w0 || p.all_partial) {
-          first = sg + w0;
-          pieces = w1 - w0 + 1;
-        }
+    for (int e = threadIdx.x; e < HG * D; e += 64 * NW) {
+      if (split == 0)
+        static_cast<T *>(a.out)[((size_t)row * a.num_q_heads + h0) * D + e] = T(0);
+      if (p.partials) {
+        p.ws_o[part * D + e] = 0.f;
+        if (e % D == 0) p.ws_lse[part + e / D] = -INFINITY;
       }
-      p.seginfo[2 * sg] = first;
-      p.seginfo[2 * sg + 1] = pieces;
     }
+    return;
   }
-  if (T_all == 0) return;
+  const int nb = max((keys + kBlock - 1) / kBlock - p.skip_blocks, 0);
+  const int b0 = p.skip_blocks + (int)((int64_t)split * nb / p.splits);
+  const int b1 = p.skip_blocks + (int)((int64_t)(split + 1) * nb / p.splits);
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform by construction; readfirstlane lets the compiler keep everything
-  // derived from it (block range, loop bounds, buffer descriptors) in scalar registers
-  // instead of wrapping each buffer load in a loop over distinct descriptor values.
+  // derived from it in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = lane % CPR;
   const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
-  const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
-  if (w >= W) return;
-  // The wave's blocks: [wb0, wb0 + nbw) in block order (possibly none).
-  const int64_t wb0 = blocks_before(quot((int64_t)w * T_cost, W));
-  const int nbw = (int)(blocks_before(quot((int64_t)(w + 1) * T_cost, W)) - wb0);
-  if (nbw == 0) return;
-  const int group = a.num_q_heads / a.num_kv_heads;
+  // This wave's blocks: b0 + wave + NW*i, i < nmine.
+  const int nmine = b1 - b0 > wave ? (b1 - b0 - wave + NW - 1) / NW : 0;
   const char *kpool = static_cast<const char *>(a.k_pool);
   const char *vpool = static_cast<const char *>(a.v_pool);
   const bool fused = !kF32 && a.k_new != nullptr;
   const char *knew = static_cast<const char *>(a.k_new);
   const char *vnew = static_cast<const char *>(a.v_new);
+  const int32_t *tbl = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
 
   // bf16: after the exchange lane `lane` < NSC owns the score of token tau_s (of the
   // current block) and head hh_s.  The softmax scale enters as |scale| with the sign
@@ -330,135 +236,73 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
   const float sc = fabsf(a.scale_log2);
   const uint32_t qflip = (!kF32 && a.scale_log2 < 0.f) ? 0x80008000u : 0u;
 
-  // State of the open piece (the wave's blocks of one segment).
-  uint32_t qw[HG][WPC];  // its query fragment: this lane's EPC dims of each head
-  uint32_t qn[HG][WPC];  // query fragment prefetched for the next piece
-  int qn_block = -1;     // wave block at which that next piece starts
-  float acc[HG][EPC];
-  float lsum[HG];   // fp32: per head, over this lane's tokens
-  float mref[HG];   // reference max per head (wave-uniform)
-  float my_m = -INFINITY;  // bf16: mref of this lane's score head
-  float my_l = 0.f;        // bf16: this lane's share of its head's weight sum
-  bool pc_open = false, pc_whole = false;
-  int pc_row = 0, pc_h0 = 0, pc_keys = 0, pc_seg = 0;
-
-  auto load_q = [&](uint32_t (&dst)[HG][WPC], int row, int h0) {
+  // Query fragment: this lane's EPC dims of each head (fp32: the scale folded in).
+  uint32_t qw[HG][WPC];
+  {
     const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
                   chunk * EPC;
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
-      dst[hh][0] = x.x ^ qflip; dst[hh][1] = x.y ^ qflip;
-      dst[hh][2] = x.z ^ qflip; dst[hh][3] = x.w ^ qflip;
-    }
-  };
-  auto head0 = [&](int g) {
-    const int kvh = g / p.num_head_groups;
-    return kvh * group + (g - kvh * p.num_head_groups) * HG;
-  };
-
-  // Totals of the open piece: the whole segment goes straight to `out`, a part of one
-  // to its partial slot (normalised o and log2-sum-exp per head).
-  auto flush = [&]() {
-    if constexpr (!kF32) {
-      // bf16: the weight sum of head hh is spread over the lanes that scored it.
+      qw[hh][0] = x.x ^ qflip; qw[hh][1] = x.y ^ qflip;
+      qw[hh][2] = x.z ^ qflip; qw[hh][3] = x.w ^ qflip;
+      if constexpr (kF32) {
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) lsum[hh] = wave_sum((scoring && hh_s == hh) ? my_l : 0.f);
-    }
-    // fp32: each token's weight was counted on all CPR lanes of the token; summing over
-    // the lanes of one chunk (one per token group) gives the piece's totals.  The
-    // accumulators of both paths hold one chunk's dims per lane and token group.
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      if constexpr (kF32) lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
-    }
-    if (lane < CPR) {
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        const float inv = lsum[hh] > 0.f ? 1.f / lsum[hh] : 0.f;
-        if (pc_whole) {
-          T *dst = static_cast<T *>(a.out) +
-                   ((size_t)pc_row * a.num_q_heads + pc_h0 + hh) * D + chunk * EPC;
-          if constexpr (kF32) {
-            *reinterpret_cast<float4 *>(dst) =
-                float4{acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv};
-          } else {
-            uint4 pk;
-            pk.x = pack_bf16x2(acc[hh][0] * inv, acc[hh][1] * inv);
-            pk.y = pack_bf16x2(acc[hh][2] * inv, acc[hh][3] * inv);
-            pk.z = pack_bf16x2(acc[hh][4] * inv, acc[hh][5] * inv);
-            pk.w = pack_bf16x2(acc[hh][6] * inv, acc[hh][7] * inv);
-            *reinterpret_cast<uint4 *>(dst) = pk;
-          }
-        } else {
-          const size_t slot = (size_t)(pc_seg + w) * HG + hh;
-          float *dst = p.ws_o + slot * D + chunk * EPC;
-#pragma unroll
-          for (int e = 0; e < EPC; e += 4)
-            *reinterpret_cast<float4 *>(dst + e) =
-                float4{acc[hh][e] * inv, acc[hh][e + 1] * inv, acc[hh][e + 2] * inv,
-                       acc[hh][e + 3] * inv};
-          if (lane == 0)
-            p.ws_lse[slot] =
-                lsum[hh] > 0.f ? mref[hh] + __builtin_amdgcn_logf(lsum[hh]) : -INFINITY;
-        }
+        for (int k = 0; k < WPC; ++k)
+          qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
       }
     }
-  };
+  }
+  float acc[HG][EPC];
+  float lsum[HG];   // fp32: per head, over this lane's tokens
+  float mref[HG];   // reference max per head (wave-uniform)
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    lsum[hh] = 0.f;
+    mref[hh] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
+  }
+  float my_m = -INFINITY;  // bf16: mref of this lane's score head
+  float my_l = 0.f;        // bf16: this lane's share of its head's weight sum
 
-  for (int c0 = 0; c0 < nbw; c0 += 64) {
-    const int nc = min(64, nbw - c0);
-    // Lane i describes wave block c0 + i: its kv-head group g, item, logical block and
-    // physical block (invalid table entries read block 0 and are masked).  All table
-    // entries of the chunk are fetched at once, whatever pieces the chunk spans.
-    int m_g = 0, m_item = 0, m_lb = 0, m_pb = 0, m_ok = 0, m_keys = 0;
-    // Item of the chunk's first block (last item with s_pref[item] <= r): a ballot
-    // over lanes for up to 64 items, else a binary search.  Each lane then walks
-    // forward from it to its own block's item; a chunk spans few items, and a lane
-    // already in the next kv-head group starts from item 0 near that group's start.
-    const int64_t b_first = wb0 + c0;
-    const int g_first = (int)quot(b_first, rows_total);
-    const int r_first = (int)(b_first - (int64_t)g_first * rows_total);
-    int it0;
-    if (p.items <= 64) {
-      it0 = 63 - __builtin_clzll(
-                     __builtin_amdgcn_ballot_w64(lane < p.items && s_pref[lane] <= r_first));
-    } else {
-      int lo = 0, hi = p.items - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] <= r_first) lo = mid; else hi = mid - 1;
-      }
-      it0 = lo;
-    }
+  // Fused write: the row's newest token (position keys-1, in block lb_new) comes from
+  // k_new / v_new, not the pool, which this launch is still writing.  The wave holding
+  // that block loads it once; the lanes of that token get the row's 16-byte chunk, all
+  // other loads are out of range and fetch nothing.
+  const int lb_new = (keys - 1) / kBlock;
+  uint4 kn{}, vn{};
+  if constexpr (!kF32) {
+    const bool has_new = fused && lb_new >= b0 && lb_new < b1 && (lb_new - b0) % NW == wave;
+    const bool mine = has_new && (keys - 1) % TPI == tok0;
+    const size_t noff = ((size_t)row * a.num_kv_heads + kvh) * D * sizeof(T);
+    const buffer_rsrc_t rkn = make_rsrc(knew + noff, has_new ? D * (int)sizeof(T) : 0);
+    const buffer_rsrc_t rvn = make_rsrc(vnew + noff, has_new ? D * (int)sizeof(T) : 0);
+    const int o = mine ? 16 * chunk : D * (int)sizeof(T);
+    kn = buffer_load16(rkn, o);
+    vn = buffer_load16(rvn, o);
+  }
+
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int nc = min(64, nmine - c0);
+    // Lane i looks up the table entry of this wave's block c0 + i (all at once);
+    // invalid entries read block 0 and are masked.
+    int m_lb = 0, m_pb = 0, m_ok = 0;
     if (lane < nc) {
-      const int64_t bi = wb0 + c0 + lane;
-      m_g = (int)quot(bi, rows_total);
-      const int r = (int)(bi - (int64_t)m_g * rows_total);
-      int lo = m_g == g_first ? it0 : 0;  // last item with s_pref[item] <= r
-      while (lo + 1 < p.items && s_pref[lo + 1] <= r) ++lo;
-      m_item = lo;
-      m_lb = r - s_pref[lo] + p.skip_blocks;
-      m_keys = s_keys[lo];
-      const int pb = a.block_tables[(size_t)s_seq[lo] * a.max_blocks_per_seq + m_lb];
+      m_lb = b0 + wave + NW * (c0 + lane);
+      const int pb = tbl[m_lb];
       m_ok = pb >= 0 && pb < a.num_blocks;
       m_pb = m_ok ? pb : 0;
     }
-    // Pieces start at a segment's first block, and at the wave's first block.
-    uint64_t starts = __builtin_amdgcn_ballot_w64(lane < nc && m_lb == p.skip_blocks);
-    if (c0 == 0) starts |= 1ull;
 
     // Raw buffer loads through a per-tile descriptor.  Prefetches past the chunk (and
     // tiles of invalid table entries) get a descriptor with no records: those loads
     // fetch nothing and return zeros, yet every path issues the same number of
     // loads, so the compiler's wait counts stay exact.
-    auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], uint4 &kn, uint4 &vn, int i) {
+    auto load = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
       const int ic = min(i, nc - 1);
       const int pb = readlane(m_pb, ic);
       const bool ok = i < nc && readlane(m_ok, ic) != 0;
-      const int kvh = readlane(m_g, ic) / p.num_head_groups;
       const size_t off = ((size_t)pb * a.num_kv_heads + kvh) * kTileBytes;
       const int nrec = ok ? kTileBytes : 0;
       const buffer_rsrc_t rk = make_rsrc(kpool + off, nrec);
@@ -467,70 +311,6 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
 #pragma unroll
       for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
-      if constexpr (!kF32) {
-        // Fused write: the lanes of a decode row's newest token (in its last block) also
-        // fetch that row from k_new / v_new; every other lane's offset is out of range,
-        // so the load fetches nothing (issued on every block to keep wait counts exact).
-        const int keys = readlane(m_keys, ic);
-        const int lb = readlane(m_lb, ic);
-        const int row = s_row[readlane(m_item, ic)];
-        const bool has_new = fused && i < nc && (keys - 1) / kBlock == lb;
-        const bool mine = has_new && (keys - 1) % TPI == tok0;
-        const size_t noff = ((size_t)row * a.num_kv_heads + kvh) * D * sizeof(T);
-        const buffer_rsrc_t rkn = make_rsrc(knew + noff, has_new ? D * (int)sizeof(T) : 0);
-        const buffer_rsrc_t rvn = make_rsrc(vnew + noff, has_new ? D * (int)sizeof(T) : 0);
-        const int o = mine ? 16 * chunk : D * (int)sizeof(T);
-        kn = buffer_load16(rkn, o);
-        vn = buffer_load16(rvn, o);
-      }
-    };
-
-    // A new piece at chunk block i: flush the open one, set up the new one, and
-    // prefetch the query of the piece after it (if that one starts in this chunk).
-    auto begin_piece = [&](int i) {
-      if (pc_open) flush();
-      const int g = readlane(m_g, i);
-      const int item = readlane(m_item, i);
-      const int lb0 = readlane(m_lb, i) - p.skip_blocks;  // first block, counted from the skip
-      pc_row = s_row[item];
-      pc_keys = s_keys[item];
-      pc_h0 = head0(g);
-      pc_seg = g * p.items + item;
-      const int n_item = s_pref[item + 1] - s_pref[item];
-      const int len = min(n_item - lb0, nbw - (c0 + i));
-      pc_whole = !p.all_partial && lb0 == 0 && len == n_item;
-      pc_open = true;
-      if (qn_block == c0 + i) {
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh)
-#pragma unroll
-          for (int k = 0; k < WPC; ++k) qw[hh][k] = qn[hh][k];
-      } else {
-        load_q(qw, pc_row, pc_h0);
-      }
-      if constexpr (kF32) {  // fold the softmax scale into q once
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh)
-#pragma unroll
-          for (int k = 0; k < WPC; ++k)
-            qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
-      }
-      const uint64_t later = i < 63 ? starts & (~0ull << (i + 1)) : 0ull;
-      if (later) {
-        const int j = __builtin_ctzll(later);
-        const int gj = readlane(m_g, j);
-        load_q(qn, s_row[readlane(m_item, j)], head0(gj));
-        qn_block = c0 + j;
-      }
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        lsum[hh] = 0.f;
-        mref[hh] = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
-      }
-      my_m = -INFINITY;
-      my_l = 0.f;
     };
 
     // bf16 block update.  Each lane forms the partial dot products of its chunk for
@@ -539,14 +319,12 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
     // is done once per score.  The weights go back through LDS as bf16, laid out so a
     // lane reads its token pairs as packed words and P.V is one dot2 per (head, dim,
     // token pair).  The denominator sums the same rounded weights.
-    auto compute_bf16 = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], const uint4 &kn,
-                            const uint4 &vn, int i, int u) {
+    auto compute_bf16 = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i, int u) {
       const int lb = readlane(m_lb, i);
       const bool bad = readlane(m_ok, i) == 0;
-      const int keys = pc_keys;
       float *red = s_red[wave][u];
       uint32_t *pw = s_pw[wave][u];
-      if (fused && (keys - 1) / kBlock == lb) {
+      if (fused && lb == lb_new) {
         // The newest token (position keys-1) comes from k_new / v_new, not the pool.
         const int jn = ((keys - 1) % kBlock) / TPI;
         const bool mine = (keys - 1) % TPI == tok0;
@@ -637,11 +415,12 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
       }
     };
 
+    // fp32 block update: per-lane fp32 dot products summed over the lanes of a token,
+    // fp32 FMAs for P.V (every lane keeps its own tokens' weights).
     auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
       const int lb = readlane(m_lb, i);
       const bool bad = readlane(m_ok, i) == 0;
       const int key0 = lb * kBlock + tok0;
-      const int keys = pc_keys;
       float s[NV][HG];
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
@@ -650,12 +429,8 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
         for (int hh = 0; hh < HG; ++hh) {
           float x = 0.f;
 #pragma unroll
-          for (int k = 0; k < WPC; ++k) {
-            if constexpr (kF32)
-              x = fmaf(__uint_as_float(qw[hh][k]), __uint_as_float(kw[k]), x);
-            else
-              x = dot2_bf16(qw[hh][k], kw[k], x);
-          }
+          for (int k = 0; k < WPC; ++k)
+            x = fmaf(__uint_as_float(qw[hh][k]), __uint_as_float(kw[k]), x);
           s[j][hh] = x;
         }
       }
@@ -666,7 +441,6 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
 #pragma unroll
         for (int hh = 0; hh < HG; ++hh) {
           float x = sum_over_token_lanes<CPR>(s[j][hh]);
-          if constexpr (!kF32) x *= a.scale_log2;
           x = valid ? x : -INFINITY;
           s[j][hh] = x;
           need |= x > mref[hh] + kRescaleSlack;
@@ -705,53 +479,95 @@ __global__ __launch_bounds__(kThreads) void decode_streamk_kernel(AttnArgs a, St
         }
 #pragma unroll
         for (int k = 0; k < WPC; ++k) {
-          if constexpr (kF32) {
-            const float x = __uint_as_float(vw[k]);
+          const float x = __uint_as_float(vw[k]);
 #pragma unroll
-            for (int hh = 0; hh < HG; ++hh) acc[hh][k] = fmaf(pr[hh], x, acc[hh][k]);
-          } else {
-            const float lo = bf16_lo(vw[k]);
-            const float hi = bf16_hi(vw[k]);
-#pragma unroll
-            for (int hh = 0; hh < HG; ++hh) {
-              acc[hh][2 * k] = fmaf(pr[hh], lo, acc[hh][2 * k]);
-              acc[hh][2 * k + 1] = fmaf(pr[hh], hi, acc[hh][2 * k + 1]);
-            }
-          }
+          for (int hh = 0; hh < HG; ++hh) acc[hh][k] = fmaf(pr[hh], x, acc[hh][k]);
         }
       }
     };
 
-    // Ring of PF+1 register buffers: while block i is computed, blocks i+1..i+PF are
-    // in flight, across piece boundaries.
-    uint4 kb[PF + 1][NV], vb[PF + 1][NV], knb[PF + 1], vnb[PF + 1];
+    // Ring of PF+1 register buffers: while block i is computed, block i+1 is in flight.
+    uint4 kb[PF + 1][NV], vb[PF + 1][NV];
 #pragma unroll
-    for (int q = 0; q < PF; ++q) load(kb[q], vb[q], knb[q], vnb[q], q);
+    for (int q = 0; q < PF; ++q) load(kb[q], vb[q], q);
     for (int i0 = 0; i0 < nc; i0 += PF + 1) {
 #pragma unroll
       for (int u = 0; u <= PF; ++u) {
         const int un = (u + PF) % (PF + 1);
-        load(kb[un], vb[un], knb[un], vnb[un], i0 + u + PF);
+        load(kb[un], vb[un], i0 + u + PF);
         const int i = i0 + u;
         if (i < nc) {
-          if ((starts >> i) & 1ull) begin_piece(i);
           if constexpr (kF32)
             compute(kb[u], vb[u], i);
           else
-            compute_bf16(kb[u], vb[u], knb[u], vnb[u], i, u);
+            compute_bf16(kb[u], vb[u], i, u);
         }
       }
     }
   }
-  if (pc_open) flush();
+
+  // The wave's totals: bf16 weight sums are spread over the lanes that scored them;
+  // fp32 counted each token's weight on all CPR lanes of the token, so summing over the
+  // lanes of one chunk gives the totals.  The accumulators hold one chunk's dims per
+  // lane and token group: summed over the token groups, lanes < CPR hold them all.
+  if constexpr (!kF32) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) lsum[hh] = wave_sum((scoring && hh_s == hh) ? my_l : 0.f);
+  }
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    if constexpr (kF32) lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
+  }
+  if (lane < CPR) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) s_o[wave][hh][chunk * EPC + e] = acc[hh][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      s_ml[wave][hh][0] = mref[hh];
+      s_ml[wave][hh][1] = lsum[hh];
+    }
+  }
+  __syncthreads();
+  // Merge of the waves: thread t owns (head t / D, dim t % D).
+  for (int t = threadIdx.x; t < HG * D; t += 64 * NW) {
+    const int hh = t / D;
+    const int d = t - hh * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, s_ml[w][hh][0]);
+    float L = 0.f, o = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float m = s_ml[w][hh][0];
+        const float wt = m == -INFINITY ? 0.f : fast_exp2(m - mx);
+        L = fmaf(wt, s_ml[w][hh][1], L);
+        o = fmaf(wt, s_o[w][hh][d], o);
+      }
+    }
+    const float res = L > 0.f ? o / L : 0.f;
+    if (p.partials) {
+      p.ws_o[(part + hh) * D + d] = res;
+      if (d == 0) p.ws_lse[part + hh] = L > 0.f ? mx + __builtin_amdgcn_logf(L) : -INFINITY;
+    } else {
+      T *dst = static_cast<T *>(a.out) + ((size_t)row * a.num_q_heads + h0 + hh) * D + d;
+      if constexpr (kF32) *dst = res;
+      else *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16(res);
+    }
+  }
 }
 
-// Log-sum-exp merge of the pieces of each segment cut across waves: with per-piece
+// Log-sum-exp merge of the key ranges of each segment cut into several: with per-range
 // (o_i, lse_i) in log2 units, out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M),
-// M = max_i lse_i.  One wave per (segment, q head of its group); the decode kernel
-// left each segment's first slot and piece count in `seginfo`.
+// M = max_i lse_i.  One wave per (segment, q head of its group).
 template <typename T, int D, int HG>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs p) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, SegArgs p) {
   constexpr bool kF32 = std::is_same<T, float>::value;
   constexpr int DW = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
@@ -761,35 +577,28 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   const int seg = gw / HG;
   const int g = seg / p.items;
   const int item = seg - g * p.items;
-  // The output row's lookup does not depend on the piece info; it is made to complete
-  // before the branch on that info (the empty asm uses it), so that both round trips
-  // overlap instead of the lookup following the branch.
   int seq, row, keys;
   bool zero;
-  item_row<kF32>(a, p.item_base + item, seq, row, keys, zero);
-  const int first = p.seginfo[2 * seg];
-  const int npieces = p.seginfo[2 * seg + 1];
-  asm volatile("" ::"s"(row));
-  if (npieces == 0) return;
+  if (!item_row<kF32>(a, item, seq, row, keys, zero) || zero) return;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int kvh = g / p.num_head_groups;
   const int h = kvh * group + (g - kvh * p.num_head_groups) * HG + hh;
-  const size_t base = (size_t)first * HG + hh;  // slot of piece i: base + i * HG
+  const size_t base = (size_t)seg * p.splits * HG + hh;  // range i: base + i * HG
 
-  // One pass in batches of 16 pieces (indices past the end are clamped to the last
-  // piece and weighted 0): each batch's lse and o values are loaded together, and the
+  // One pass in batches of 16 ranges (indices past the end are clamped to the last
+  // range and weighted 0): each batch's lse and o values are loaded together, and the
   // running sums are rescaled when the running maximum rises.
   constexpr int kBatch = 16;
   float M = -INFINITY, L = 0.f;
   float o[DW];
 #pragma unroll
   for (int e = 0; e < DW; ++e) o[e] = 0.f;
-  for (int s0 = 0; s0 < npieces; s0 += kBatch) {
+  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
     float v[kBatch][DW];
     float lv[kBatch];
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
-      const int j = min(s0 + jj, npieces - 1);
+      const int j = min(s0 + jj, p.splits - 1);
       const size_t slot = base + (size_t)j * HG;
       lv[jj] = p.ws_lse[slot];
       const float *src = p.ws_o + slot * D;
@@ -799,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
     float bm = M;
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj)
-      if (s0 + jj < npieces) bm = fmaxf(bm, lv[jj]);
+      if (s0 + jj < p.splits) bm = fmaxf(bm, lv[jj]);
     if (bm == -INFINITY) continue;  // nothing with weight yet
     const float r = (M == -INFINITY) ? 0.f : fast_exp2(M - bm);
     L *= r;
@@ -808,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
     M = bm;
 #pragma unroll
     for (int jj = 0; jj < kBatch; ++jj) {
-      const float wj = (s0 + jj < npieces && lv[jj] != -INFINITY) ? fast_exp2(lv[jj] - M) : 0.f;
+      const float wj = (s0 + jj < p.splits && lv[jj] != -INFINITY) ? fast_exp2(lv[jj] - M) : 0.f;
       L += wj;
 #pragma unroll
       for (int e = 0; e < DW; ++e) o[e] = fmaf(wj, v[jj][e], o[e]);
@@ -823,38 +632,37 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, StreamArgs 
   }
 }
 
-template <typename T, int D, int HG, int PF>
+template <typename T, int D, int HG, int NW>
 static hipError_t launch_decode_t(const AttnArgs &a, const DecodePlan &pl, hipStream_t st) {
-  for (int base = 0; base < pl.items; base += kMaxStreamItems) {
-    StreamArgs p{};
-    p.item_base = base;
-    p.items = min(kMaxStreamItems, pl.items - base);
-    p.num_head_groups = pl.num_head_groups;
-    p.groups = a.num_kv_heads * pl.num_head_groups;
+  SegArgs p{};
+  p.items = pl.items;
+  p.num_head_groups = pl.num_head_groups;
+  p.groups = a.num_kv_heads * pl.num_head_groups;
+  p.splits = pl.splits;
+  p.skip_blocks = pl.skip_blocks;
+  p.partials = (pl.splits > 1 || pl.cascade) ? 1 : 0;
+  if (p.partials) {
     p.ws_o = reinterpret_cast<float *>(static_cast<char *>(pl.workspace) + pl.ws_o_offset);
     p.ws_lse = reinterpret_cast<float *>(static_cast<char *>(pl.workspace) + pl.ws_lse_offset);
-    p.seginfo =
-        reinterpret_cast<int *>(static_cast<char *>(pl.workspace) + pl.ws_seginfo_offset);
-    p.skip_blocks = pl.skip_blocks;
-    p.all_partial = pl.cascade ? 1 : 0;
-
-    decode_streamk_kernel<T, D, HG, PF><<<dim3(pl.grid), dim3(kThreads), 0, st>>>(a, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (pl.cascade) continue;  // one launch (at most kMaxStreamItems rows); merged later
-    const int waves = p.items * p.groups * HG;
-    merge_kernel<T, D, HG><<<dim3((waves + kWaves - 1) / kWaves), dim3(kThreads), 0, st>>>(
-        a, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  const int64_t wgs = (int64_t)p.items * p.groups * p.splits;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  decode_kernel<T, D, HG, NW><<<dim3((unsigned)wgs), dim3(64 * NW), 0, st>>>(a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.splits == 1 || pl.cascade) return e;
+  const int64_t waves = (int64_t)p.items * p.groups * HG;
+  merge_kernel<T, D, HG><<<dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(kThreads), 0,
+                           st>>>(a, p);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int HG>
-static hipError_t launch_decode_p(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
-  if (p.prefetch != 1) return hipErrorInvalidValue;
-  return launch_decode_t<T, D, HG, 1>(a, p, st);
+static hipError_t launch_decode_w(const AttnArgs &a, const DecodePlan &p, hipStream_t st) {
+  if constexpr (!std::is_same<T, float>::value) {  // fp32 rows always take 8 waves
+    if (p.waves == kDecodeWavesMax) return launch_decode_t<T, D, HG, kDecodeWavesMax>(a, p, st);
+  }
+  if (p.waves == kDecodeWavesMin) return launch_decode_t<T, D, HG, kDecodeWavesMin>(a, p, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
@@ -862,12 +670,12 @@ static hipError_t launch_decode_d(const AttnArgs &a, const DecodePlan &p, hipStr
   // Only the head groups the planner can pick for this element type and head_dim.
   constexpr int kMaxHG = (512 / (D * (int)sizeof(T))) < 4 ? (512 / (D * (int)sizeof(T))) : 4;
   switch (p.head_group) {
-    case 1: return launch_decode_p<T, D, 1>(a, p, st);
+    case 1: return launch_decode_w<T, D, 1>(a, p, st);
     case 2:
-      if constexpr (kMaxHG >= 2) return launch_decode_p<T, D, 2>(a, p, st);
+      if constexpr (kMaxHG >= 2) return launch_decode_w<T, D, 2>(a, p, st);
       break;
     case 4:
-      if constexpr (kMaxHG >= 4) return launch_decode_p<T, D, 4>(a, p, st);
+      if constexpr (kMaxHG >= 4) return launch_decode_w<T, D, 4>(a, p, st);
       break;
   }
   return hipErrorInvalidValue;

@@ -69,30 +69,33 @@ int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context
 // Decode (single-query rows) plan.
 //
 // Work items ("rows") are sequences with one query (bf16) or every query row (fp32,
-// where prefill rows also take this path).  The decode kernel is persistent: `grid`
-// workgroups of 4 waves split the concatenated blocks of all (kv-head group, row)
-// segments into equal contiguous ranges, one per wave (stream-K).  Pieces of segments
-// cut across waves go to workspace slots that the merge kernel combines.  Rows are
-// handled kMaxStreamItems at a time (one decode + merge launch per chunk).
+// where prefill rows also take this path).  A segment is (row, kv-head group).  Its
+// blocks are cut into `splits` contiguous key ranges, one workgroup each, whose waves
+// take the range's blocks in turn and merge their states in LDS.  With one range per
+// segment the workgroup writes the output; otherwise each range leaves a normalised
+// partial (o, log2-sum-exp) and a merge kernel combines them.
 // ---------------------------------------------------------------------------
-constexpr int kMaxStreamItems = 2048;
+constexpr int kDecodeWavesMax = 16;  // waves per decode workgroup: 16 when the
+constexpr int kDecodeWavesMin = 8;   // segments fit the compute units one each, else 8
+constexpr int kBlocksPerWave = 16;   // blocks a wave may take before segments split
 
 struct DecodePlan {
   int items;            // work rows: num_seqs (bf16) or total_q (fp32)
   int group;            // G = num_q_heads / num_kv_heads
   int head_group;       // q heads handled together by one wave (divides G)
   int num_head_groups;  // G / head_group
-  int prefetch;         // blocks in flight per wave while one is computed (1)
-  int grid;             // persistent decode workgroups
+  int waves;            // waves per workgroup (kDecodeWavesMax or kDecodeWavesMin)
+  int splits;           // key ranges (workgroups) per segment
   int skip_blocks;      // leading blocks of every row left out (a shared prefix), or 0
-  bool cascade;         // every segment leaves a partial; no merge launch (the shared-
+  bool cascade;         // partials even with one range, no merge launch (the shared-
                         // prefix merge combines them with the shared run's partials)
-  size_t ws_o_offset, ws_lse_offset, ws_seginfo_offset, ws_bytes;
+  size_t ws_o_offset, ws_lse_offset, ws_bytes;
   void *workspace;      // set by the caller before launching
 };
 
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
-                       int head_dim, int max_context_len, pkv_dtype dtype);
+                       int head_dim, int max_context_len, pkv_dtype dtype,
+                       int skip_blocks = 0, bool cascade = false);
 
 struct AttnArgs {
   void *out;
@@ -115,15 +118,15 @@ struct AttnArgs {
 };
 
 // Per-launch arguments of the decode and merge kernels.
-struct StreamArgs {
-  int item_base, items;  // rows [item_base, item_base + items) of this launch
+struct SegArgs {
+  int items;             // work rows
   int num_head_groups;   // G / head_group
   int groups;            // num_kv_heads * num_head_groups
-  float *ws_o;           // [slot][head_group][D] normalised partial outputs
-  float *ws_lse;         // [slot][head_group] log2-sum-exp of each partial
-  int *seginfo;          // [segments][2]: first partial slot, piece count (0: none)
+  int splits;            // key ranges per segment
   int skip_blocks;       // leading logical blocks of every row this launch leaves out
-  int all_partial;       // nonzero: segments finished in one wave also leave a partial
+  int partials;          // nonzero: every range writes its partial instead of `out`
+  float *ws_o;           // [segment][range][head_group][D] normalised partial outputs
+  float *ws_lse;         // [segment][range][head_group] log2-sum-exp (-inf: no key)
 };
 
 // Launchers (return hipSuccess or the launch error).

@@ -192,10 +192,11 @@ def attention_with_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
 
 
 def shared_prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
-                                 head_dim: int, shared_blocks: int,
+                                 head_dim: int, max_context_len: int, shared_blocks: int,
                                  dtype: torch.dtype = torch.bfloat16) -> int:
     return int(_lib.load().paged_attention_shared_prefix_workspace_size(
-        num_seqs, num_q_heads, num_kv_heads, head_dim, shared_blocks, _DTYPES[dtype]))
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, shared_blocks,
+        _DTYPES[dtype]))
 
 
 def attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -248,7 +249,8 @@ def attention_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
         _on_gpu("out", out, dev)
         _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if workspace is None:
-        need = shared_prefix_workspace_size(num_seqs, hq, hkv, d, shared_blocks, q.dtype) \
+        need = shared_prefix_workspace_size(num_seqs, hq, hkv, d, max_context_len,
+                                            shared_blocks, q.dtype) \
             if shared_blocks > 0 else \
             (workspace_size(num_seqs, total_q, hq, hkv, d, max_context_len, q.dtype)
              if num_seqs and total_q else 0)

@@ -190,7 +190,8 @@ void validator_and_arguments() {
                                 0.125f, PKV_BF16, p, 64, nullptr) == PKV_OK);
   EXPECT(paged_kv_write(p, p, p, p, slots, 2, 8, 4, 96, 16, PKV_BF16, nullptr) ==
          PKV_ERR_UNSUPPORTED);
-  EXPECT(paged_attention_workspace_size(32, 32, 32, 8, 64, 2048, PKV_BF16) > 0);
+  EXPECT(paged_attention_workspace_size(32, 32, 32, 8, 64, 2048, PKV_BF16) == 0);
+  EXPECT(paged_attention_workspace_size(32, 32, 32, 8, 64, 9000, PKV_BF16) > 0);
   EXPECT(paged_attention_workspace_size(32, 32, 30, 8, 64, 2048, PKV_BF16) == 0);
   for (int s = -1; s < 8; ++s) EXPECT(pkv_status_string((pkv_status)s) != nullptr);
   // The fused call's positional slots: row 0 is position 19 (table block 1 = physical
@@ -217,7 +218,7 @@ void validator_and_arguments() {
                                               qsl, 2, 2, 8, 4, 30, 1, 1, 8, 4, 64, 16,
                                               0.125f, PKV_BF16, p, 64, nullptr) ==
          PKV_ERR_WORKSPACE);
-  EXPECT(paged_attention_shared_prefix_workspace_size(2, 8, 4, 64, 1, PKV_BF16) > 64);
+  EXPECT(paged_attention_shared_prefix_workspace_size(2, 8, 4, 64, 30, 1, PKV_BF16) > 64);
   // The no-alloc call: a batch beyond its scratch is refused before any device call.
   EXPECT(paged_attention_varlen_with_write_noalloc(p, p, p, p, p, p, slots, bt, ctx, qsl, 1,
                                                    32512, 8, 4, 32512, 32512, 1, 1, 128, 16,

@@ -99,16 +99,27 @@ def test_attention_argument_checks(over, want):
 
 
 def test_workspace_size_plan():
+    """Decode rows need scratch only where a segment (row, kv-head group) is cut into
+    several key ranges: when one range would give a wave more than 8 blocks, or when
+    the segments alone cannot fill the GPU's 256 compute units (the answer without a
+    GPU).  Chunks add scratch where their tiles are split over the key range."""
     lib = _lib.load()
     ws = lib.paged_attention_workspace_size
-    small = ws(4, 4, 4, 2, 64, 64, _lib.PKV_F32)
-    assert small > 0                                           # row prefix + partial slots
-    big = ws(32, 32, 32, 8, 64, 2048, _lib.PKV_BF16)
-    assert big > 0
-    # grows with rows and heads; fp32 items are query rows, bf16 items are sequences
-    assert ws(64, 64, 32, 8, 64, 2048, _lib.PKV_BF16) > big
-    assert ws(32, 2048, 32, 8, 64, 2048, _lib.PKV_F32) > ws(32, 2048, 32, 8, 64, 2048,
-                                                             _lib.PKV_BF16)
+    # 32 x 8 segments of <= 128 blocks: one workgroup each, outputs written directly.
+    assert ws(32, 32, 32, 8, 64, 2048, _lib.PKV_BF16) == 0
+    assert ws(34, 34, 16, 8, 128, 640, _lib.PKV_BF16) == 0
+    # longer rows are cut into key ranges (partials + merge)
+    long1 = ws(32, 32, 32, 8, 64, 2049 + 2047, _lib.PKV_BF16)
+    assert long1 > 0
+    assert ws(64, 64, 32, 8, 64, 4096, _lib.PKV_BF16) > long1   # grows with rows
+    # few segments: ranges to fill the GPU
+    assert ws(2, 2, 8, 2, 64, 2048, _lib.PKV_BF16) > 0
+    few = ws(2, 2, 8, 2, 64, 2048, _lib.PKV_F32)
+    assert few > 0
+    assert ws(2, 8, 8, 2, 64, 2048, _lib.PKV_F32) > few         # fp32 items are rows
+    assert ws(1, 1, 2, 1, 64, 33001, _lib.PKV_F32) > 0
+    # a chunk with few tiles over a long context: split partials
+    assert ws(1, 40, 16, 8, 128, 6000, _lib.PKV_BF16) > 0
     assert ws(0, 0, 32, 8, 64, 2048, _lib.PKV_BF16) == 0
     assert ws(4, 4, 6, 4, 64, 2048, _lib.PKV_BF16) == 0       # invalid heads
 
@@ -184,7 +195,6 @@ def test_shared_prefix_argument_checks_and_validator():
     assert call(dtype=_lib.PKV_F32) == _lib.PKV_ERR_UNSUPPORTED
     assert call(max_q=2) == _lib.PKV_ERR_UNSUPPORTED
     assert call(total_q=3) == _lib.PKV_ERR_UNSUPPORTED
-    assert call(num_seqs=2049, total_q=2049) == _lib.PKV_ERR_UNSUPPORTED
     assert call(d=96) == _lib.PKV_ERR_UNSUPPORTED
     assert call(bs=8) == _lib.PKV_ERR_UNSUPPORTED
     assert call(shared=-1) == _lib.PKV_ERR_INVALID_ARG
@@ -193,10 +203,10 @@ def test_shared_prefix_argument_checks_and_validator():
     assert call(ws_bytes=16) == _lib.PKV_ERR_WORKSPACE
     assert call(num_seqs=0, total_q=0) == _lib.PKV_OK
     ws = lib.paged_attention_shared_prefix_workspace_size
-    assert ws(32, 16, 8, 128, 187, _lib.PKV_BF16) > 0
-    assert ws(32, 16, 8, 128, 0, _lib.PKV_BF16) == 0
-    assert ws(32, 16, 8, 128, 187, _lib.PKV_F32) == 0
-    assert ws(2049, 16, 8, 128, 187, _lib.PKV_BF16) == 0
+    assert ws(32, 16, 8, 128, 3160, 187, _lib.PKV_BF16) > 0
+    assert ws(32, 16, 8, 128, 3160, 0, _lib.PKV_BF16) == 0
+    assert ws(32, 16, 8, 128, 3160, 187, _lib.PKV_F32) == 0
+    assert ws(32, 16, 8, 128, -1, 187, _lib.PKV_BF16) == 0
 
     b = make_config("shared_prefix_decode", 0)
     args = (b.block_tables, b.context_lens, b.query_start_loc)

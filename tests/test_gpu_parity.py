@@ -373,9 +373,14 @@ def test_one_hot_probe_bit_exact(dtype, q_len):
 # ---------------------------------------------------------------------------
 
 def test_workspace_too_small_is_an_error():
+    """A batch whose rows are cut into several key ranges needs scratch for their
+    partials: a smaller workspace is refused before any launch."""
     import paged_kv_cache_290_amd as pkv
 
-    b = make_config("llama32_1b_decode", 0)
+    b = _case("long_needs_workspace", 0, dtype="bf16", num_q_heads=16, num_kv_heads=8,
+              head_dim=128, num_blocks=600, context_lens=[9000, 20], query_lens=[1, 1])
+    assert pkv.workspace_size(b.num_seqs, b.total_q, 16, 8, 128, b.max_context_len,
+                              torch.bfloat16) > 16
     db = DeviceBatch(b)
     tiny = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(pkv.PagedKVError) as ei:

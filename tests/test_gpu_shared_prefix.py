@@ -103,8 +103,8 @@ def test_cascade_agrees_with_the_plain_call_and_reuses_its_workspace():
     bs = [make_config("shared_prefix_decode", s) for s in (3, 4)]
     bs.append(_shared_case(5, 16, 8, 128, 100, [3, 90, 17]))
     shared = [187, 187, 100]
-    need = max(pkv.shared_prefix_workspace_size(b.num_seqs, 16, 8, 128, sh)
-               for b, sh in zip(bs, shared))
+    need = max(pkv.shared_prefix_workspace_size(b.num_seqs, 16, 8, 128, b.max_context_len,
+                                                sh) for b, sh in zip(bs, shared))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     dbs = [DeviceBatch(b) for b in bs]
     for db in dbs:
