@@ -186,12 +186,47 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   const int item = (int)(v % p.items);
   const int g = (int)(v / p.items);
   const int seg = g * p.items + item;
-  int seq, row, keys;
-  bool zero;
-  if (!item_row<kF32>(a, item, seq, row, keys, zero)) return;  // not a decode row
   const int group = a.num_q_heads / a.num_kv_heads;
   const int kvh = g / p.num_head_groups;
   const int h0 = kvh * group + (g - kvh * p.num_head_groups) * HG;
+  const int lane = threadIdx.x & 63;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep everything
+  // derived from it in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int chunk = lane % CPR;
+  const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
+  const uint32_t qflip = (!kF32 && a.scale_log2 < 0.f) ? 0x80008000u : 0u;
+
+  // bf16 items are sequences, so the table row is known before any load: with one key
+  // range per segment this wave's first blocks are skip + wave + NW*i, and their table
+  // entries are requested together with the row's lengths (one round trip less before
+  // the first K/V request).  Likewise the query is fetched from row `item`, the row of
+  // every sequence in a batch of decode rows only, and fetched again below if the
+  // batch says otherwise.
+  const bool early_tbl = !kF32 && p.splits == 1;
+  int early_pb = 0;
+  if (early_tbl) {
+    const int lb = p.skip_blocks + wave + NW * lane;
+    if (lb < a.max_blocks_per_seq)
+      early_pb = a.block_tables[(size_t)item * a.max_blocks_per_seq + lb];
+  }
+  uint32_t qw[HG][WPC];
+  auto load_q = [&](int r) {
+    const T *qp = static_cast<const T *>(a.q) + ((size_t)r * a.num_q_heads + h0) * D +
+                  chunk * EPC;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
+      qw[hh][0] = x.x ^ qflip; qw[hh][1] = x.y ^ qflip;
+      qw[hh][2] = x.z ^ qflip; qw[hh][3] = x.w ^ qflip;
+    }
+  };
+  const int row_guess = min(item, a.total_q - 1);
+  if constexpr (!kF32) load_q(row_guess);
+
+  int seq, row, keys;
+  bool zero;
+  if (!item_row<kF32>(a, item, seq, row, keys, zero)) return;  // not a decode row
   const size_t part = ((size_t)seg * p.splits + split) * HG;  // partial slot of head 0
   if (zero) {
     // Rows of sequences that break q_len <= context_len: defined as zeros.
@@ -209,12 +244,6 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   const int b0 = p.skip_blocks + (int)((int64_t)split * nb / p.splits);
   const int b1 = p.skip_blocks + (int)((int64_t)(split + 1) * nb / p.splits);
 
-  const int lane = threadIdx.x & 63;
-  // Wave-uniform by construction; readfirstlane lets the compiler keep everything
-  // derived from it in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int chunk = lane % CPR;
-  const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
   // This wave's blocks: b0 + wave + NW*i, i < nmine.
   const int nmine = b1 - b0 > wave ? (b1 - b0 - wave + NW - 1) / NW : 0;
   const char *kpool = static_cast<const char *>(a.k_pool);
@@ -234,24 +263,17 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   const int tau_s = TPI * j_s + (lane - k_s * TPI);
   const bool scoring = lane < NSC;
   const float sc = fabsf(a.scale_log2);
-  const uint32_t qflip = (!kF32 && a.scale_log2 < 0.f) ? 0x80008000u : 0u;
 
   // Query fragment: this lane's EPC dims of each head (fp32: the scale folded in).
-  uint32_t qw[HG][WPC];
-  {
-    const T *qp = static_cast<const T *>(a.q) + ((size_t)row * a.num_q_heads + h0) * D +
-                  chunk * EPC;
+  if constexpr (kF32) {
+    load_q(row);
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const uint4 x = *reinterpret_cast<const uint4 *>(qp + hh * D);
-      qw[hh][0] = x.x ^ qflip; qw[hh][1] = x.y ^ qflip;
-      qw[hh][2] = x.z ^ qflip; qw[hh][3] = x.w ^ qflip;
-      if constexpr (kF32) {
+    for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-        for (int k = 0; k < WPC; ++k)
-          qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
-      }
-    }
+      for (int k = 0; k < WPC; ++k)
+        qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
+  } else if (row != row_guess) {
+    load_q(row);
   }
   float acc[HG][EPC];
   float lsum[HG];   // fp32: per head, over this lane's tokens
@@ -290,7 +312,7 @@ void decode_kernel(AttnArgs a, SegArgs p) {
     int m_lb = 0, m_pb = 0, m_ok = 0;
     if (lane < nc) {
       m_lb = b0 + wave + NW * (c0 + lane);
-      const int pb = tbl[m_lb];
+      const int pb = (early_tbl && c0 == 0) ? early_pb : tbl[m_lb];
       m_ok = pb >= 0 && pb < a.num_blocks;
       m_pb = m_ok ? pb : 0;
     }
