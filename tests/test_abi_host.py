@@ -100,7 +100,7 @@ def test_attention_argument_checks(over, want):
 
 def test_workspace_size_plan():
     """Decode rows need scratch only where a segment (row, kv-head group) is cut into
-    several key ranges: when one range would give a wave more than 8 blocks, or when
+    several key ranges: when one range would give a wave more than 16 blocks, or when
     the segments alone cannot fill the GPU's 256 compute units (the answer without a
     GPU).  Chunks add scratch where their tiles are split over the key range."""
     lib = _lib.load()
@@ -108,10 +108,12 @@ def test_workspace_size_plan():
     # 32 x 8 segments of <= 128 blocks: one workgroup each, outputs written directly.
     assert ws(32, 32, 32, 8, 64, 2048, _lib.PKV_BF16) == 0
     assert ws(34, 34, 16, 8, 128, 640, _lib.PKV_BF16) == 0
-    # longer rows are cut into key ranges (partials + merge)
-    long1 = ws(32, 32, 32, 8, 64, 2049 + 2047, _lib.PKV_BF16)
+    # 16 waves x 16 blocks = 4,096 keys still fit one range; longer rows are cut
+    # into key ranges (partials + merge)
+    assert ws(32, 32, 32, 8, 64, 4096, _lib.PKV_BF16) == 0
+    long1 = ws(32, 32, 32, 8, 64, 4097, _lib.PKV_BF16)
     assert long1 > 0
-    assert ws(64, 64, 32, 8, 64, 4096, _lib.PKV_BF16) > long1   # grows with rows
+    assert ws(64, 64, 32, 8, 64, 4097, _lib.PKV_BF16) > long1   # grows with rows
     # few segments: ranges to fill the GPU
     assert ws(2, 2, 8, 2, 64, 2048, _lib.PKV_BF16) > 0
     few = ws(2, 2, 8, 2, 64, 2048, _lib.PKV_F32)
