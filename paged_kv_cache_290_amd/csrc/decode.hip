@@ -29,6 +29,14 @@
 // max per head; the reference is raised only when some score exceeds it by more than
 // kRescaleSlack (then every lane rescales), so the usual per-block cross-lane max is
 // replaced by one ballot.  Terms stay below 2^kRescaleSlack, far from fp32 overflow.
+//
+// bf16 tiles with head_dim 64 run both products of a block on the matrix cores: the
+// scores as S^T = K Q^T (v_mfma_f32_16x16x32_bf16: 16 tokens x 16 columns, the
+// group's HG heads in the first columns), whose accumulator layout is the B operand
+// layout of the second product O^T += V^T P^T (v_mfma_f32_16x16x16_bf16), so the
+// weights stay in the lanes that computed them; V^T comes from the wave's V tile in
+// LDS through transposing reads.  Each column keeps its own lazily raised reference.
+// The other cases use packed bf16 dot products (v_dot2_f32_bf16) or fp32 FMAs.
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -52,6 +60,26 @@ struct DecodeMap {
   static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
   static constexpr int WPC = 4;                 // dwords per chunk
 };
+
+// Matrix-core path (bf16, head_dim 64), lane l = 16 * lg + l16.  MFMA operand layout:
+// A row l16 and B column l16 each hold the k-slots (lg, e); the accumulator holds rows
+// 4 lg .. 4 lg + 3 of column l16.  K tiles are loaded straight into A fragments
+// (token l16, dims 32 j + 8 lg .. + 7 for load j); V tiles go to LDS row-major, each
+// row's 32-byte chunk pairs permuted by vslot so that the 8 rows that one transposing
+// read pass touches fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int vslot(int t, int c) {
+  const int f = D == 64 ? ((t >> 1) & 3) : (t & 7);
+  return c ^ (2 * f);
+}
+
+__device__ __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_k16(v4i16_t a, v4i16_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
 // Sum over the CPR lanes of a token (lanes l with equal l / CPR).
 template <int CPR>
@@ -139,13 +167,17 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   constexpr int CPR = M::CPR, TPI = M::TPI, NV = M::NV, EPC = M::EPC, WPC = M::WPC;
   constexpr int kTileBytes = kBlock * D * (int)sizeof(T);
   constexpr int PF = 1;  // blocks in flight per wave while one is computed
+  constexpr bool kMfma = !kF32 && D == 64;  // both products on the matrix cores
+  constexpr int MT = D / 16;                // 16-dim tiles of O^T (matrix-core path)
 
-  // bf16 path: per wave and ring slot, partial scores [j*HG + hh][lane] and the bf16
-  // weights [token group][head][j] exchanged between the lanes of the wave.
-  constexpr int kRed = kF32 ? 1 : NV * HG * 64;
-  constexpr int kPw = kF32 ? 1 : 16 * HG / 2;
+  // bf16 dot-product path: per wave and ring slot, partial scores [j*HG + hh][lane] and
+  // the bf16 weights [token group][head][j] exchanged between the lanes of the wave.
+  constexpr int kRed = (kF32 || kMfma) ? 1 : NV * HG * 64;
+  constexpr int kPw = (kF32 || kMfma) ? 1 : 16 * HG / 2;
   __shared__ float s_red[NW][PF + 1][kRed];
   __shared__ uint32_t s_pw[NW][PF + 1][kPw];
+  // Matrix-core path: each wave's current V tile (rows permuted by vslot).
+  __shared__ uint4 s_v[kMfma ? NW * kTileBytes / 16 : 1];
   // The waves' states for the merge: unnormalised outputs, reference max, weight sum.
   __shared__ float s_o[NW][HG][D];
   __shared__ float s_ml[NW][HG][2];
@@ -195,6 +227,8 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = lane % CPR;
   const int tok0 = lane / CPR;  // token of load j is TPI*j + tok0
+  const int l16 = lane & 15;    // matrix-core path: token (K) or column (head) of the lane
+  const int lg = lane >> 4;
   const uint32_t qflip = (!kF32 && a.scale_log2 < 0.f) ? 0x80008000u : 0u;
 
   // bf16 items are sequences, so the table row is known before any load: with one key
@@ -221,8 +255,22 @@ void decode_kernel(AttnArgs a, SegArgs p) {
       qw[hh][2] = x.z ^ qflip; qw[hh][3] = x.w ^ qflip;
     }
   };
+  // Matrix-core path: Q^T fragments, column l16 = head h0 + l16 (zeros past the group's
+  // HG heads), dims 32 j + 8 lg .. + 7.
+  uint4 qf[NV];
+  auto load_qf = [&](int r) {
+    const T *qp = static_cast<const T *>(a.q) +
+                  ((size_t)r * a.num_q_heads + h0 + min(l16, HG - 1)) * D + 8 * lg;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      uint4 x = *reinterpret_cast<const uint4 *>(qp + 32 * j);
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+      qf[j] = l16 < HG ? x : uint4{0u, 0u, 0u, 0u};
+    }
+  };
   const int row_guess = min(item, a.total_q - 1);
-  if constexpr (!kF32) load_q(row_guess);
+  if constexpr (kMfma) load_qf(row_guess);
+  else if constexpr (!kF32) load_q(row_guess);
 
   int seq, row, keys;
   bool zero;
@@ -273,7 +321,8 @@ void decode_kernel(AttnArgs a, SegArgs p) {
       for (int k = 0; k < WPC; ++k)
         qw[hh][k] = __float_as_uint(__uint_as_float(qw[hh][k]) * a.scale_log2);
   } else if (row != row_guess) {
-    load_q(row);
+    if constexpr (kMfma) load_qf(row);
+    else load_q(row);
   }
   float acc[HG][EPC];
   float lsum[HG];   // fp32: per head, over this lane's tokens
@@ -285,8 +334,12 @@ void decode_kernel(AttnArgs a, SegArgs p) {
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
   }
-  float my_m = -INFINITY;  // bf16: mref of this lane's score head
+  float my_m = -INFINITY;  // bf16: mref of this lane's score head (column)
   float my_l = 0.f;        // bf16: this lane's share of its head's weight sum
+  float mneg = 0.f;        // matrix-core path: -my_m, or 0 while my_m is -inf
+  f32x4_t oacc[kMfma ? MT : 1];  // matrix-core path: O^T tiles (dims 16 mt + 4 lg + r)
+#pragma unroll
+  for (int mt = 0; mt < (kMfma ? MT : 1); ++mt) oacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Fused write: the row's newest token (position keys-1, in block lb_new) comes from
   // k_new / v_new, not the pool, which this launch is still writing.  The wave holding
@@ -330,7 +383,8 @@ void decode_kernel(AttnArgs a, SegArgs p) {
       const buffer_rsrc_t rk = make_rsrc(kpool + off, nrec);
       const buffer_rsrc_t rv = make_rsrc(vpool + off, nrec);
 #pragma unroll
-      for (int j = 0; j < NV; ++j) kr[j] = buffer_load16(rk, 1024 * j + 16 * lane);
+      for (int j = 0; j < NV; ++j)
+        kr[j] = buffer_load16(rk, kMfma ? l16 * M::R + 64 * j + 16 * lg : 1024 * j + 16 * lane);
 #pragma unroll
       for (int j = 0; j < NV; ++j) vr[j] = buffer_load16(rv, 1024 * j + 16 * lane);
     };
@@ -437,6 +491,87 @@ void decode_kernel(AttnArgs a, SegArgs p) {
       }
     };
 
+    // Matrix-core block update (bf16, head_dim 64).  The weights are rounded to bf16 for
+    // P.V and the denominator sums the same rounded values.  Columns past the group's
+    // heads score 0 and accumulate harmless sums that are never stored.
+    auto compute_mfma = [&](uint4 (&kr)[NV], uint4 (&vr)[NV], int i) {
+      const int lb = readlane(m_lb, i);
+      const bool bad = readlane(m_ok, i) == 0;
+      char *vt = reinterpret_cast<char *>(s_v) + wave * kTileBytes;
+      if (fused && lb == lb_new) {
+        // The newest token comes from k_new / v_new, not the pool.  Its K chunks sit in
+        // the lanes of kn that load it (token tn % TPI of the load layout); the A-layout
+        // lanes of token tn fetch them from there.
+        const int tn = (keys - 1) % kBlock;
+        const int src = (tn % TPI) * CPR;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int sl = (src + 4 * j + lg) * 4;
+          uint4 x;
+          x.x = __builtin_amdgcn_ds_bpermute(sl, (int)kn.x);
+          x.y = __builtin_amdgcn_ds_bpermute(sl, (int)kn.y);
+          x.z = __builtin_amdgcn_ds_bpermute(sl, (int)kn.z);
+          x.w = __builtin_amdgcn_ds_bpermute(sl, (int)kn.w);
+          if (l16 == tn) kr[j] = x;
+        }
+        const int jn = tn / TPI;
+        const bool mine = tn % TPI == tok0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          if (j == jn && mine) vr[j] = vn;
+      }
+      // V tile to LDS; slots past the context (and tiles of invalid blocks) may hold
+      // anything, including NaN: they become 0 (their weight is 0).
+      const bool edge = bad || (lb + 1) * kBlock > keys;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int t = TPI * j + tok0;
+        uint4 x = vr[j];
+        if (edge && (bad || lb * kBlock + t >= keys)) x = uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4 *>(vt + t * M::R + vslot<D>(t, chunk) * 16) = x;
+      }
+      // S^T = K Q^T: lane (lg, l16) holds tokens 4 lg + r of column l16.
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NV; ++j) sacc = mfma_k32(kr[j], qf[j], sacc);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = sacc[r] * sc;
+        if (edge && (bad || lb * kBlock + 4 * lg + r >= keys)) x[r] = -INFINITY;
+      }
+      const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (wave_any(m4 > my_m + kRescaleSlack)) {
+        // Raise the reference of every column to its new maximum (over the four lane
+        // groups that share the column).
+        float mc = fmaxf(m4, shfl_xor(m4, 16));
+        mc = fmaxf(mc, shfl_xor(mc, 32));
+        const float mn = fmaxf(my_m, mc);
+        const float alpha = (my_m == -INFINITY) ? 0.f : fast_exp2(my_m - mn);
+        my_m = mn;
+        mneg = (mn == -INFINITY) ? 0.f : -mn;
+        my_l *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
+      }
+      const uint32_t pk0 = pack_bf16x2(fast_exp2(x[0] + mneg), fast_exp2(x[1] + mneg));
+      const uint32_t pk1 = pack_bf16x2(fast_exp2(x[2] + mneg), fast_exp2(x[3] + mneg));
+      my_l = dot2_bf16(pk0, 0x3F803F80u, my_l);
+      my_l = dot2_bf16(pk1, 0x3F803F80u, my_l);
+      const v4i16_t pb = __builtin_bit_cast(v4i16_t, uint2{pk0, pk1});
+      // O^T += V^T P^T: the transposing read gives lane (lg, i) dim 16 mt + i of tokens
+      // 4 lg + 0..3; lane (lg, 4 jj + q) addresses token 4 lg + jj, dims 16 mt + 4 q..+3.
+      const int vt_tok = 4 * lg + (l16 >> 2);
+      const int vt_q = l16 & 3;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const v4i16_t av = lds_read_tr16(vt + vt_tok * M::R +
+                                         vslot<D>(vt_tok, 2 * mt + (vt_q >> 1)) * 16 +
+                                         (vt_q & 1) * 8);
+        oacc[mt] = mfma_k16(av, pb, oacc[mt]);
+      }
+    };
+
     // fp32 block update: per-lane fp32 dot products summed over the lanes of a token,
     // fp32 FMAs for P.V (every lane keeps its own tokens' weights).
     auto compute = [&](const uint4 (&kr)[NV], const uint4 (&vr)[NV], int i) {
@@ -521,6 +656,8 @@ void decode_kernel(AttnArgs a, SegArgs p) {
         if (i < nc) {
           if constexpr (kF32)
             compute(kb[u], vb[u], i);
+          else if constexpr (kMfma)
+            compute_mfma(kb[u], vb[u], i);
           else
             compute_bf16(kb[u], vb[u], i, u);
         }
@@ -532,27 +669,45 @@ void decode_kernel(AttnArgs a, SegArgs p) {
   // fp32 counted each token's weight on all CPR lanes of the token, so summing over the
   // lanes of one chunk gives the totals.  The accumulators hold one chunk's dims per
   // lane and token group: summed over the token groups, lanes < CPR hold them all.
-  if constexpr (!kF32) {
+  if constexpr (kMfma) {
+    // Column l16's totals: the weight sum over its four lane groups; its O^T tiles hold
+    // dims 16 mt + 4 lg + r.
+    float lt = my_l + shfl_xor(my_l, 16);
+    lt += shfl_xor(lt, 32);
+    if (l16 < HG) {
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) lsum[hh] = wave_sum((scoring && hh_s == hh) ? my_l : 0.f);
-  }
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    if constexpr (kF32) lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
+        for (int r = 0; r < 4; ++r) s_o[wave][l16][16 * mt + 4 * lg + r] = oacc[mt][r];
+      if (lg == 0) {
+        s_ml[wave][l16][0] = my_m;
+        s_ml[wave][l16][1] = lt;
+      }
+    }
+  } else {
+    if constexpr (!kF32) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
-  }
-  if (lane < CPR) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) s_o[wave][hh][chunk * EPC + e] = acc[hh][e];
-  }
-  if (lane == 0) {
+      for (int hh = 0; hh < HG; ++hh)
+        lsum[hh] = wave_sum((scoring && hh_s == hh) ? my_l : 0.f);
+    }
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      s_ml[wave][hh][0] = mref[hh];
-      s_ml[wave][hh][1] = lsum[hh];
+      if constexpr (kF32) lsum[hh] = sum_over_chunk_lanes<CPR>(lsum[hh]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
+    }
+    if (lane < CPR) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s_o[wave][hh][chunk * EPC + e] = acc[hh][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        s_ml[wave][hh][0] = mref[hh];
+        s_ml[wave][hh][1] = lsum[hh];
+      }
     }
   }
   __syncthreads();

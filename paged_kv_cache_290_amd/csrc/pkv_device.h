@@ -9,6 +9,7 @@ namespace pkv {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // bf16 is carried as raw 16-bit storage.  Widening is exact: the 16 bits are the top
 // half of a float32.
@@ -56,6 +57,14 @@ __device__ __forceinline__ float wave_max_over_quads(float x) {
   x = fmaxf(x, shfl_xor(x, 16));
   x = fmaxf(x, shfl_xor(x, 32));
   return x;
+}
+
+// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16).  Within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed by lanes
+// 4j + i / 4 of the group, j = 0..3 (element j of the result from row j).
+__device__ __forceinline__ v4i16_t lds_read_tr16(const void *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t *)(p));
 }
 
 __device__ __forceinline__ bool wave_any(bool p) {

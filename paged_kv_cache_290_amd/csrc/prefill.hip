@@ -74,15 +74,7 @@ __device__ __forceinline__ void load_lds16(const void *g, uint32_t lds_byte) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_byte));
 }
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
-
-// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16; lane mapping
-// stated where it is used).
-__device__ __forceinline__ v4i16_t lds_read_tr16(const void *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16_t *)(p));
-}
 
 // Slot of 16-byte chunk c of a K row in LDS: c ^ swz_k(row), of a V row: c ^
 // swz_v(row).  Both depend on the row mod 16 only (every row that one thread stages
