@@ -29,7 +29,7 @@ Timing
     read and stored, and its slot indices.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                       [--only-main] [--only-chunk] [--only-scaling]
+                       [--only-main] [--only-chunk] [--only-scaling] [--only-long]
                        [--only-achievable] [--only-mixed] [--only-chunk-sweep]
 """
 from __future__ import annotations
@@ -271,57 +271,84 @@ class DeviceRunner(Runner):
                    for _ in sets]
 
 
-def measure_batch_scaling(steps: int, warmup: int) -> dict:
-    """Context for the headline: the same decode shape (Llama-3.2-1B heads, 32q/8kv,
-    d=64, contexts U[128, 2048], bf16) at batches 32, 128 and 512, drawn on the device
-    (torch generator seeded by the batch size; no oracle is involved: these are the
-    kernels the parity tests cover).  A call has fixed costs — the launch, the
-    metadata scan and table walk before the first K/V bytes arrive, the merge launch —
-    that weigh less as the bytes per step grow.  Same protocol as the headline: fused
-    steps in one HIP graph over rotating copies (>= 1 GiB in total)."""
+def _device_decode_case(ctx, steps: int, warmup: int, seed: int) -> dict:
+    """One fused decode step over Llama-3.2-1B heads (32q/8kv, d=64, bf16) with the
+    context lengths `ctx` (a CPU int tensor), drawn on the device with a torch
+    generator seeded by `seed` (no oracle is involved: these are the kernels the
+    parity tests cover).  Same protocol as the headline: fused steps in one HIP graph
+    over rotating copies (>= 1 GiB in total)."""
     import types
 
     import torch
 
-    hq, hkv, d, mb = 32, 8, 64, 128
+    hq, hkv, d = 32, 8, 64
+    batch = int(ctx.numel())
+    g = torch.Generator().manual_seed(seed)
+    nblk = (ctx + 15) // 16
+    mb = int(nblk.max())
+    nb = max(8192, batch * mb)
+    tbl = torch.randperm(nb, generator=g)[: batch * mb].view(batch, mb).to(torch.int32)
+    tbl[torch.arange(mb).view(1, -1) >= nblk.view(-1, 1)] = -1
+    last = ctx - 1
+    slot = tbl[torch.arange(batch), last // 16].long() * 16 + last % 16
+    b = types.SimpleNamespace(
+        num_seqs=batch, total_q=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        max_context_len=int(ctx.max()), max_query_len=1, scale=d ** -0.5)
+    kv = int(ctx.sum()) * hkv * d * 2 * 2
+    per = (kv + 2 * batch * hq * d * 2 + int(nblk.sum()) * 4 + 8 * batch + 4 +
+           2 * 2 * batch * hkv * d * 2 + 4 * batch)
+    rot = max(2, min(32, math.ceil(ROTATE_BYTES / per)))
+    sets = []
+    for _ in range(rot):
+        s = types.SimpleNamespace()
+        s.k_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
+        s.v_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
+        s.q = torch.randn(batch, hq, d, device="cuda").to(torch.bfloat16)
+        s.k_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
+        s.v_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
+        s.block_tables = tbl.cuda()
+        s.context_lens = ctx.to(torch.int32).cuda()
+        s.query_start_loc = torch.arange(batch + 1, dtype=torch.int32, device="cuda")
+        s.slot_mapping = slot.to(torch.int32).cuda()
+        sets.append(s)
+    r = DeviceRunner(b, sets)
+    ms = time_graph(r, steps, warmup)
+    ws = r.pkv.workspace_size(batch, batch, hq, hkv, d, int(ctx.max()), torch.bfloat16)
+    gbs = per / (ms * 1e-3) / 1e9
+    res = {"bytes_per_step": per, "rotating_copies": rot, "ms_per_step": round(ms, 5),
+           "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "key_ranges": ws > 0}
+    del r, sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_batch_scaling(steps: int, warmup: int) -> dict:
+    """Context for the headline: the same decode shape (Llama-3.2-1B heads, 32q/8kv,
+    d=64, contexts U[128, 2048], bf16) at batches 32, 128 and 512.  A call has fixed
+    costs — the launch, the table walk before the first K/V bytes arrive, the
+    segments' unequal lengths — that weigh less as the bytes per step grow."""
+    import torch
+
     res = {}
     for batch in (32, 128, 512):
         g = torch.Generator().manual_seed(batch)
         ctx = torch.randint(128, 2049, (batch,), generator=g)
-        nb = max(8192, batch * mb)
-        nblk = (ctx + 15) // 16
-        tbl = torch.randperm(nb, generator=g)[: batch * mb].view(batch, mb).to(torch.int32)
-        tbl[torch.arange(mb).view(1, -1) >= nblk.view(-1, 1)] = -1
-        last = ctx - 1
-        slot = tbl[torch.arange(batch), last // 16].long() * 16 + last % 16
-        b = types.SimpleNamespace(
-            num_seqs=batch, total_q=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-            max_context_len=int(ctx.max()), max_query_len=1, scale=d ** -0.5)
-        kv = int(ctx.sum()) * hkv * d * 2 * 2
-        per = (kv + 2 * batch * hq * d * 2 + int(nblk.sum()) * 4 + 8 * batch + 4 +
-               2 * 2 * batch * hkv * d * 2 + 4 * batch)
-        rot = max(2, min(32, math.ceil(ROTATE_BYTES / per)))
-        sets = []
-        for _ in range(rot):
-            s = types.SimpleNamespace()
-            s.k_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
-            s.v_pool = torch.randn(nb, hkv, 16, d, device="cuda").to(torch.bfloat16)
-            s.q = torch.randn(batch, hq, d, device="cuda").to(torch.bfloat16)
-            s.k_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
-            s.v_new = torch.randn(batch, hkv, d, device="cuda").to(torch.bfloat16)
-            s.block_tables = tbl.cuda()
-            s.context_lens = ctx.to(torch.int32).cuda()
-            s.query_start_loc = torch.arange(batch + 1, dtype=torch.int32, device="cuda")
-            s.slot_mapping = slot.to(torch.int32).cuda()
-            sets.append(s)
-        r = DeviceRunner(b, sets)
-        ms = time_graph(r, steps, warmup)
-        gbs = per / (ms * 1e-3) / 1e9
-        res[f"batch_{batch}"] = {"bytes_per_step": per, "rotating_copies": rot,
-                                 "ms_per_step": round(ms, 5), "GBs": round(gbs, 1),
-                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        del r, sets
-        torch.cuda.empty_cache()
+        res[f"batch_{batch}"] = _device_decode_case(ctx, steps, warmup, batch)
+    return res
+
+
+def measure_long_context(steps: int, warmup: int) -> dict:
+    """Context: decode over long contexts with the same heads (Llama-3.2-1B, bf16), where
+    each (sequence, kv head) segment is cut into key ranges whose partial results the
+    merge kernel combines: 4 sequences of 32,768 tokens and 1 of 131,072 (~268 MB of
+    K/V per step each), beside 64 sequences of 2,048 (the same bytes, no key ranges)."""
+    import torch
+
+    res = {}
+    for batch, c in ((4, 32768), (1, 131072), (64, 2048)):
+        ctx = torch.full((batch,), c, dtype=torch.int64)
+        res[f"{batch}x{c}"] = _device_decode_case(ctx, steps, warmup, 7 * batch + 1)
     return res
 
 
@@ -1011,6 +1038,8 @@ def main() -> int:
                     help="only the measured HBM read and bf16 GEMM ceilings")
     ap.add_argument("--only-scaling", action="store_true",
                     help="only the headline decode shape at batches 32, 128 and 512")
+    ap.add_argument("--only-long", action="store_true",
+                    help="only the long-context decode leg (key ranges + merge)")
     ap.add_argument("--only-shared", action="store_true",
                     help="only the shared-prefix workload, plain and cascade (profiling)")
     ap.add_argument("--only-chunk", action="store_true",
@@ -1096,6 +1125,11 @@ def main() -> int:
 
     if args.only_achievable:
         print(json.dumps({"achievable": measure_achievable(args.steps)}))
+        return 0
+
+    if args.only_long:
+        print(json.dumps({"decode_long_context": measure_long_context(args.steps,
+                                                                      args.warmup)}))
         return 0
 
     if args.only_scaling:
@@ -1195,6 +1229,8 @@ def main() -> int:
         result["workloads"] = extra
         log("timing the headline decode shape at larger batches")
         result["decode_batch_scaling"] = measure_batch_scaling(args.steps, args.warmup)
+        log("timing long-context decode (key ranges + merge)")
+        result["decode_long_context"] = measure_long_context(args.steps, args.warmup)
         log("timing the chunk kernel at several step budgets")
         result["chunk_budget_sweep"] = measure_chunk_sweep(args.steps)
         log("measuring achievable HBM read and bf16 GEMM rates")
