@@ -100,9 +100,11 @@ __device__ __forceinline__ int swz_v(int row) {
 // One wave's update with a 64-key tile: kb and vb = K and V tiles, each row-major
 // [key][16-byte chunk slot] (slots as above); kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
-// position or past kv_end).
-template <int D, bool MASK>
-__device__ __forceinline__ void tile_update(const uint4 *kb, const uint4 *vb,
+// position or past kv_end).  mid(ks) is called after the score products of k-step ks
+// (the caller issues one part of the next step's staging there, so that the staging
+// loads do not stall the wave in one burst ahead of the products).
+template <int D, bool MASK, typename FM>
+__device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uint4 *vb,
                                             const bf16x8_t (&qf)[2][D / 32],
                                             f32x4_t (&o)[D / 16][2], float (&mref)[2],
                                             float (&mneg)[2], float (&lsum)[2], float sc,
@@ -127,6 +129,7 @@ __device__ __forceinline__ void tile_update(const uint4 *kb, const uint4 *vb,
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) sacc[sub][cg] = mfma16(af, qf[cg][ks], sacc[sub][cg]);
     }
+    mid(ks);
   }
 
   // Per-lane maximum of the scaled scores (log2 units).
@@ -456,7 +459,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       PKV_FILL_TBL((st + 1) * (kStepKeys / kBlock));
       __syncthreads();
     }
-    if (st + 1 < nst) PKV_FETCH(st + 1, buf ^ 1);  // in flight during this step
+    // The staging of step st+1 (into the buffer step st-1 used, free since the last
+    // barrier) in KCH parts, one per k-step of this step's score products; KCH equals
+    // the number of k-steps (D / 32).
+    static_assert(KCH == KS, "one staging part per k-step");
+    const bool fetch_next = st + 1 < nst;
+    const int fb0 = ((st + 1) * (kStepKeys / kBlock)) % kTblCache;
+    auto fetch_part = [&](int i) {
+      if (fetch_next) {
+        const uint64_t off_ =
+            (uint64_t)(uint32_t)s_tbl[fb0 + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;
+        const int key_ = kw0 + KSTRIDE * i;
+        const int row_ = ((buf ^ 1) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH;
+        load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));
+        load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));
+      }
+    };
 
     const int kbase = st * kStepKeys + half * kHalfKeys;
     if (kbase < kv_end) {
@@ -464,11 +482,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
       const uint4 *vb = v_lds + (buf * 2 + half) * K_U4;
       const bool edge = (kbase + kHalfKeys - 1 > pos_first) || (kbase + kHalfKeys > kv_end);
       if (edge)
-        tile_update<D, true>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
-                             l16, lg);
+        tile_update<D, true>(fetch_part, kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos,
+                             kv_end, l16, lg);
       else
-        tile_update<D, false>(kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos, kv_end,
-                              l16, lg);
+        tile_update<D, false>(fetch_part, kb, vb, qf, o, mref, mneg, lsum, sc, kbase, col_pos,
+                              kv_end, l16, lg);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) fetch_part(i);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step st+1 have landed
     if (st + 1 < nst) PKV_ZERO_TAIL(st + 1, buf ^ 1);
