@@ -88,10 +88,12 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
 
 /*
  * paged_attention_workspace_size -- bytes of device scratch that
- * paged_attention_varlen needs for the same arguments on the current device (0 only
- * for an empty batch or invalid shapes).  It holds the split-K partial results and a
- * small descriptor per (row, kv-head group); its size depends on the
- * device's compute-unit count.  The shape arguments must match the later call.
+ * paged_attention_varlen needs for the same arguments on the current device.  It
+ * holds the partial results of decode segments cut into key ranges (long rows, or too
+ * few segments to fill the device) and of prefill chunks split over their keys; it is
+ * 0 when nothing is split (e.g. 32 decode rows of up to 4,096 keys), for an empty
+ * batch and for invalid shapes.  Its size depends on the device's compute-unit count.
+ * The shape arguments must match the later call.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,
                                       int32_t num_q_heads, int32_t num_kv_heads,
@@ -185,10 +187,10 @@ pkv_status paged_attention_varlen_with_write(
  *                  (contents need no initialisation).
  * Supported: bf16, one query row per sequence (max_query_len == 1, total_q ==
  * num_seqs); other shapes give PKV_ERR_UNSUPPORTED before any launch (use the plain
- * entry points).  The workspace query takes the call's max_context_len.  Three launches on `stream`: the decode kernel
- * over each row's own blocks (leaving partial results), the MFMA chunk kernel over the
- * shared blocks with every row as a column (leaving partial results per key split),
- * and a merge per (row, query head).
+ * entry points).  The workspace query takes the call's max_context_len.  Three
+ * launches on `stream`: the decode kernel over each row's own blocks (leaving partial
+ * results), the MFMA chunk kernel over the shared blocks with every row as a column
+ * (leaving partial results per key split), and a merge per (row, query head).
  */
 size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
