@@ -91,7 +91,8 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
  * paged_attention_varlen needs for the same arguments on the current device.  It
  * holds the partial results of decode segments cut into key ranges (long rows, or too
  * few segments to fill the device) and of prefill chunks split over their keys; it is
- * 0 when nothing is split (e.g. 32 decode rows of up to 4,096 keys), for an empty
+ * 0 when nothing is split (e.g. 32 bf16 decode rows with 8 kv heads and up to 4,096
+ * keys each, on a 256-CU device), for an empty
  * batch and for invalid shapes.  Its size depends on the device's compute-unit count.
  * The shape arguments must match the later call.
  */
