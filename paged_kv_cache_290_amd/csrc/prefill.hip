@@ -132,11 +132,10 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
     mid(ks);
   }
 
-  // Per-lane maximum of the scaled scores (log2 units).
-  float lmx[2];
+  // Masked scores (MASK: past a column's position or past kv_end) become -inf.
+  if (MASK) {
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
-    if (MASK) {
+    for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
@@ -144,7 +143,26 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
           const int key = kbase + sub * 16 + 4 * lg + r;
           if (key > col_pos[cg] || key >= kv_end) sacc[sub][cg][r] = -INFINITY;
         }
-    }
+  }
+  // P = exp2(s * sc - mref), first with the current reference: the exponentials need
+  // only this step's scores, so they can issue while the last score products finish
+  // and before the reference check below.  Where that check raises the reference (it
+  // does whenever a score exceeds the reference by more than kSlack, in particular on
+  // a wave's first keys), the weights are recomputed; otherwise every weight is at most
+  // 2^kSlack.
+  float p[2][16];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        p[cg][sub * 4 + r] = fast_exp2(fmaf(sacc[sub][cg][r], sc, mneg[cg]));
+
+  // Per-lane maximum of the scaled scores (log2 units).
+  float lmx[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
     float m = sacc[0][cg][0];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub)
@@ -167,26 +185,25 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
       lsum[cg] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[mt][cg] *= alpha;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          p[cg][sub * 4 + r] = fast_exp2(fmaf(sacc[sub][cg][r], sc, mneg[cg]));
     }
   }
 
-  // P = exp2(s * sc - mref), bf16 packed in the k-slot order of the V^T fragments.
+  // P in bf16, packed in the k-slot order of the V^T fragments.
   bf16x8_t pf[2][2];
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg) {
-    float p[16];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        p[sub * 4 + r] = fast_exp2(fmaf(sacc[sub][cg][r], sc, mneg[cg]));
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       uint4 packed;
-      packed.x = pack_bf16x2(p[8 * ks2 + 0], p[8 * ks2 + 1]);
-      packed.y = pack_bf16x2(p[8 * ks2 + 2], p[8 * ks2 + 3]);
-      packed.z = pack_bf16x2(p[8 * ks2 + 4], p[8 * ks2 + 5]);
-      packed.w = pack_bf16x2(p[8 * ks2 + 6], p[8 * ks2 + 7]);
+      packed.x = pack_bf16x2(p[cg][8 * ks2 + 0], p[cg][8 * ks2 + 1]);
+      packed.y = pack_bf16x2(p[cg][8 * ks2 + 2], p[cg][8 * ks2 + 3]);
+      packed.z = pack_bf16x2(p[cg][8 * ks2 + 4], p[cg][8 * ks2 + 5]);
+      packed.w = pack_bf16x2(p[cg][8 * ks2 + 6], p[cg][8 * ks2 + 7]);
       pf[cg][ks2] = as_bf16x8(packed);
       // The denominator sums the same bf16-rounded weights the numerator uses.
       lsum[cg] = dot2_bf16(packed.x, kBf16Ones, lsum[cg]);
