@@ -478,19 +478,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     }
     // The staging of step st+1 (into the buffer step st-1 used, free since the last
     // barrier) in KCH parts, one per k-step of this step's score products; KCH equals
-    // the number of k-steps (D / 32).
+    // the number of k-steps (D / 32).  The last step stages too, without a branch
+    // around each part: the table cache then names blocks of the current window (or
+    // block 0), so those loads read valid pool rows into the buffer no step reads any
+    // more, and they have landed before the barrier that ends the loop.
     static_assert(KCH == KS, "one staging part per k-step");
-    const bool fetch_next = st + 1 < nst;
     const int fb0 = ((st + 1) * (kStepKeys / kBlock)) % kTblCache;
     auto fetch_part = [&](int i) {
-      if (fetch_next) {
-        const uint64_t off_ =
-            (uint64_t)(uint32_t)s_tbl[fb0 + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;
-        const int key_ = kw0 + KSTRIDE * i;
-        const int row_ = ((buf ^ 1) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH;
-        load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));
-        load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));
-      }
+      const uint64_t off_ =
+          (uint64_t)(uint32_t)s_tbl[fb0 + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;
+      const int key_ = kw0 + KSTRIDE * i;
+      const int row_ = ((buf ^ 1) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH;
+      load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));
+      load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));
     };
 
     const int kbase = st * kStepKeys + half * kHalfKeys;
