@@ -28,7 +28,7 @@ struct CascadeArgs {
   // shared-run splits
   const float *sh_o;     // [tile][split][column][D]
   const float *sh_lse;   // [tile][split][column]
-  int sh_hg, sh_nhg, sh_tile_slots, sh_splits;
+  int sh_hg, sh_nhg, sh_splits;
 };
 
 constexpr int kBatch = 8;  // parts whose loads are issued together
@@ -61,9 +61,10 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(AttnArgs a, Cas
     return;
   }
   const size_t dbase = (size_t)seg * c.dec_splits * c.dec_hg + (w % c.dec_hg);
-  // Shared splits: the row is column (w % sh_hg) * bm + row % bm of tile slot row / bm.
+  // Shared splits: the row is column (w % sh_hg) * bm + row % bm of row tile row / bm.
   const int bm = kPrefillCols / c.sh_hg;
-  const int tile = (kvh * c.sh_nhg + w / c.sh_hg) * c.sh_tile_slots + row / bm;
+  const int tile = prefill_tile_index(row / bm, kvh * c.sh_nhg + w / c.sh_hg,
+                                      a.num_kv_heads * c.sh_nhg);
   const size_t sbase = (size_t)tile * c.sh_splits * kPrefillCols + (w % c.sh_hg) * bm + row % bm;
   const int nparts = npieces + c.sh_splits;
 
@@ -135,7 +136,6 @@ hipError_t launch_cascade_merge(const AttnArgs &a, const DecodePlan &dp, const P
   c.sh_lse = reinterpret_cast<const float *>(sw + sp.ws_lse_offset);
   c.sh_hg = sp.head_group;
   c.sh_nhg = sp.num_head_groups;
-  c.sh_tile_slots = sp.tile_slots;
   c.sh_splits = sp.splits;
   const int waves = a.num_seqs * a.num_q_heads;
   const dim3 grid((waves + kWaves - 1) / kWaves);

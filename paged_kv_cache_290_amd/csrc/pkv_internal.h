@@ -181,11 +181,17 @@ hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &p, int shared
 hipError_t launch_cascade_merge(const AttnArgs &a, const DecodePlan &dp,
                                 const PrefillPlan &sp, hipStream_t stream);
 
-// Work-slot count of the prefill launch: an upper bound on the number of query tiles
-// over all sequences (each sequence's tiles fit between floor(qsl[s]/BM) + s and the
-// next sequence's start).
+// Row-tile count bound of the prefill launch: the sequences' ceil(q_len / BM) row tiles
+// add up to at most floor(total_q / BM) plus one per sequence.
 inline int prefill_tile_slots(int total_q, int num_seqs, int rows_per_tile) {
   return total_q / rows_per_tile + num_seqs;
+}
+
+// Index of the prefill tile of row tile j and head unit h (kv head * head groups + head
+// group) among `units` head units: row tiles are the slow index, so with the tiles
+// launched in index order every XCD's real tiles come before the empty slots.
+__host__ __device__ inline int prefill_tile_index(int j, int h, int units) {
+  return j * units + h;
 }
 
 }  // namespace pkv

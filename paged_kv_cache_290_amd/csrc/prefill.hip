@@ -97,6 +97,57 @@ __device__ __forceinline__ int swz_v(int row) {
   else return (row & 2) | (((row ^ (row >> 2)) & 1) << 2);
 }
 
+// Row tiles of a batch: a sequence with q_len >= 2 query rows (q_len <= total_q) has
+// ceil(q_len / BM) of them, numbered over the sequences in order; decode rows and
+// broken lengths have none.  Finds the sequence of row tile j and j's index among that
+// sequence's tiles (seq = -1 when j is past the last one).  Every thread of the
+// workgroup calls it (two barriers): thread t counts the tiles of a run of
+// ceil(num_seqs / threads) consecutive sequences, an exclusive scan over the threads
+// finds the run holding j, and that thread walks it.
+template <int BM>
+__device__ __forceinline__ void find_row_tile(const int32_t *qsl, int num_seqs, int total_q,
+                                              int j, int *s_find, int &seq, int &local) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int kW = kPThreads / 64;
+  auto tiles_of = [&](int s) {
+    const int q = qsl[s + 1] - qsl[s];
+    return (q >= 2 && q <= total_q) ? (q + BM - 1) / BM : 0;
+  };
+  const int per = (num_seqs + kPThreads - 1) / kPThreads;
+  const int s0 = min(tid * per, num_seqs);
+  const int s1 = min(s0 + per, num_seqs);
+  int cnt = 0;
+  for (int s = s0; s < s1; ++s) cnt += tiles_of(s);
+  int inc = cnt;  // inclusive prefix over the wave's lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) s_find[wave] = inc;
+  if (tid == 0) s_find[kW] = -1;
+  __syncthreads();
+  int excl = inc - cnt;
+  for (int w = 0; w < wave; ++w) excl += s_find[w];
+  if (j >= excl && j < excl + cnt) {
+    int r = j - excl;
+    for (int s = s0; s < s1; ++s) {
+      const int n = tiles_of(s);
+      if (r < n) {
+        s_find[kW] = s;
+        s_find[kW + 1] = r;
+        break;
+      }
+      r -= n;
+    }
+  }
+  __syncthreads();
+  seq = s_find[kW];
+  local = s_find[kW + 1];
+}
+
 // One wave's update with a 64-key tile: kb and vb = K and V tiles, each row-major
 // [key][16-byte chunk slot] (slots as above); kbase = position of the tile's first key.  MASK
 // applies the causal and length masks (tiles that reach past the first column's
@@ -258,6 +309,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   static_assert(4 * XF * 64 * 4 <= LDS_U4 * 16, "merge exchange must fit the tiles");
   __shared__ uint4 lds[LDS_U4];
   __shared__ int s_tbl[kTblCache];  // block-table entries of this workgroup
+  __shared__ int s_find[kPThreads / 64 + 2];  // row-tile lookup
   uint4 *const k_lds = lds;             // [buf*2+half][K_U4]
   uint4 *const v_lds = lds + 4 * K_U4;  // [buf*2+half][K_U4]
 
@@ -268,49 +320,50 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  const int total = tile_slots * a.num_kv_heads * num_head_groups * ps.splits;
-  int v = xcd_remap(blockIdx.x, gridDim.x);
-  if (v >= total) return;
-  // The splits of one tile are consecutive workgroups (one XCD, shared K/V in its L2).
-  const int split = v % ps.splits;
-  v /= ps.splits;
-  const int tile = v;
+  // Workgroup u computes split u % splits of tile u / splits, and tile = row tile j *
+  // units + head unit (prefill_tile_index), the row tiles numbered densely (below).
+  // Workgroups go to the XCDs round-robin by index and, inside an XCD, to its shader
+  // engines round-robin, each waiting for a free compute unit of its own engine.  With
+  // dense numbering every XCD starts its real tiles first, spread over all its engines
+  // (with an empty slot after each real tile, as a batch of 64-row chunks had when the
+  // tiles were numbered by query offset, the real tiles all fell on two of the four
+  // engines and ran in two rounds, taking twice as long).
+  const int units = a.num_kv_heads * num_head_groups;
+  const int total = tile_slots * units * ps.splits;
+  const int u = blockIdx.x;
+  if (u >= total) return;
+  const int split = u % ps.splits;
+  const int tile = u / ps.splits;
   const int tid = threadIdx.x;
   const bool shared = ps.shared_keys > 0;  // the shared-run pass of a shared prefix
   const bool partials = ps.splits > 1 || shared;
   // Split partials: until this tile's columns are known, mark them all unused, so the
   // merge skips tiles that end early (decode rows, empty slots, broken lengths).
   if (partials && split == 0 && tid < kCols) ps.col[(size_t)tile * kCols + tid] = -1;
-  const int slot = v % tile_slots;
-  v /= tile_slots;
-  const int hgi = v % num_head_groups;
-  const int kvh = v / num_head_groups;
+  const int j = tile / units;
+  const int hu = tile - j * units;
+  const int hgi = hu % num_head_groups;
+  const int kvh = hu / num_head_groups;
 
   int seq, q_begin, q_len, qtile, ctx;
   if (shared) {
     // Every row of the batch is a column of one chunk over the shared run (table row
-    // 0's first blocks); slot t holds rows [t*BMQ, (t+1)*BMQ).
+    // 0's first blocks); row tile j holds rows [j*BMQ, (j+1)*BMQ).
     seq = 0;
     q_begin = 0;
     q_len = a.total_q;
-    if (slot * BMQ >= q_len) return;
-    qtile = slot;
+    if (j * BMQ >= q_len) return;
+    qtile = j;
     ctx = ps.shared_keys;
   } else {
-    // Sequence owning this tile slot: the last s with qsl[s]/BMQ + s <= slot.
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.query_start_loc[mid] / BMQ + mid <= slot) lo = mid; else hi = mid - 1;
-    }
-    seq = lo;
+    // Decode rows (one query) have no row tile: they run in the split-K kernel.
+    int local;
+    find_row_tile<BMQ>(a.query_start_loc, a.num_seqs, a.total_q, j, s_find, seq, local);
+    if (seq < 0) return;  // past the batch's last row tile
     q_begin = a.query_start_loc[seq];
     q_len = a.query_start_loc[seq + 1] - q_begin;
-    if (q_len <= 1) return;  // decode rows run in the split-K kernel
     if (q_begin < 0 || q_begin + q_len > a.total_q) return;
     const int ntiles = (q_len + BMQ - 1) / BMQ;
-    const int local = slot - (q_begin / BMQ + seq);
-    if (local >= ntiles) return;
     qtile = ntiles - 1 - local;  // tiles that see the most keys go first
     ctx = a.context_lens[seq];
   }
@@ -633,9 +686,8 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
     ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
   }
-  const int grid = ((total + 7) / 8) * 8;
-  prefill_mfma_kernel<D, HGP><<<dim3(grid), dim3(kPThreads), 0, st>>>(a, pl.num_head_groups,
-                                                                       pl.tile_slots, ps);
+  prefill_mfma_kernel<D, HGP><<<dim3(total), dim3(kPThreads), 0, st>>>(a, pl.num_head_groups,
+                                                                        pl.tile_slots, ps);
   hipError_t e = hipGetLastError();
   // A shared run's partials are merged with the rows' other parts elsewhere.
   if (e != hipSuccess || pl.splits == 1 || shared_keys > 0) return e;
