@@ -94,6 +94,9 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
  * 0 when nothing is split (e.g. 32 bf16 decode rows with 8 kv heads and up to 4,096
  * keys each, on a 256-CU device), for an empty
  * batch and for invalid shapes.  Its size depends on the device's compute-unit count.
+ * For bf16 batches of several sequences with more query rows than sequences (so
+ * holding a chunk) it also covers the key ranges of the decode rows when they run in
+ * the chunk launch (8-wave workgroups: rows past 2,048 keys are cut into ranges).
  * The shape arguments must match the later call.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,
@@ -155,7 +158,11 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
  * (block_tables[s][pos / 16] * 16 + pos % 16).  With that, bf16 single-token rows
  * read their newest key and value straight from k_new / v_new while the same kernel
  * stores all new rows, saving the separate write launch.  Other cases run the write
- * kernel first.  Arguments as for the two calls above (k_new, v_new [total_q][Hkv][D]).
+ * kernel first; so do bf16 batches of several sequences with more query rows than
+ * sequences, whose chunk tiles and decode rows then share one attention launch (the
+ * decode rows in the workgroups after the chunk tiles, filling the compute units that
+ * the chunk's shorter row tiles free).  Arguments as for the two calls above (k_new,
+ * v_new [total_q][Hkv][D]).
  */
 pkv_status paged_attention_varlen_with_write(
     void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,

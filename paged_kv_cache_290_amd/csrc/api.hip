@@ -43,7 +43,7 @@ static int device_cus() {
 
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
                        int head_dim, int max_context_len, pkv_dtype dtype, int skip_blocks,
-                       bool cascade) {
+                       bool cascade, bool mixed) {
   DecodePlan p{};
   p.group = num_q_heads / num_kv_heads;
   p.head_group = pick_head_group(p.group, head_dim, dtype);
@@ -58,7 +58,9 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
   // waves of 256 registers, one workgroup per unit.
   const int64_t segments = (int64_t)p.items * num_kv_heads * p.num_head_groups;
   const int64_t cus = device_cus();
-  p.waves = (dtype == PKV_BF16 && segments <= cus) ? kDecodeWavesMax : kDecodeWavesMin;
+  // Decode rows of a mixed launch run in the chunk kernel's 8-wave workgroups.
+  p.waves = (dtype == PKV_BF16 && segments <= cus && !mixed) ? kDecodeWavesMax
+                                                              : kDecodeWavesMin;
   // Key ranges per segment: one, unless a wave would take more than kBlocksPerWave
   // blocks of the longest row, or the segments alone leave compute units idle (then
   // as many as fill them, each range keeping a block per wave or more).
@@ -133,11 +135,21 @@ PrefillPlan plan_shared_run(int total_q, int num_q_heads, int num_kv_heads, int 
 
 // Workspace bytes one attention call uses: the decode partials, and after them the
 // split-chunk partials when the batch may hold chunks (bf16 rows of q_len >= 2).
+// A bf16 batch of several sequences with more query rows than sequences holds a chunk
+// (q_len >= 2) and may hold decode rows: it runs as one mixed launch, the chunk tiles
+// first and the decode rows in the workgroups after them.  (Batches with as many rows
+// as sequences keep separate launches, so that the workspace of a decode batch does not
+// depend on whether it could also hold chunks.)
+static bool mixed_batch(int num_seqs, int total_q, int max_query_len, pkv_dtype dtype) {
+  return dtype == PKV_BF16 && max_query_len > 1 && num_seqs > 1 && total_q > num_seqs;
+}
+
 static size_t required_workspace(int num_seqs, int total_q, int num_q_heads,
                                  int num_kv_heads, int head_dim, int max_context_len,
                                  int max_query_len, pkv_dtype dtype) {
-  const DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads,
-                                      head_dim, max_context_len, dtype);
+  const DecodePlan plan =
+      plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                  dtype, 0, false, mixed_batch(num_seqs, total_q, max_query_len, dtype));
   if (!(dtype == PKV_BF16 && max_query_len > 1)) return plan.ws_bytes;
   return plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                       max_context_len, dtype, plan.ws_bytes)
@@ -184,10 +196,16 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q, int32_t
       num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype) ||
       max_context_len < 0)
     return 0;
-  // Decode partials first, then the partials of split prefill chunks.
-  const size_t dec = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                                 max_context_len, dtype)
-                         .ws_bytes;
+  // Decode partials first (for a batch that can be mixed, the larger of the plain and
+  // the mixed plan: the query does not know max_query_len), then the partials of split
+  // prefill chunks.
+  size_t dec = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                           max_context_len, dtype)
+                   .ws_bytes;
+  if (mixed_batch(num_seqs, total_q, 2, dtype))
+    dec = std::max(dec, plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
+                                    max_context_len, dtype, 0, false, true)
+                            .ws_bytes);
   return plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                       max_context_len, dtype, dec)
       .ws_end;
@@ -222,8 +240,9 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
   const bool with_write = k_new != nullptr;
   if (with_write && (!v_new || !slot_mapping)) return PKV_ERR_INVALID_ARG;
 
+  const bool mixed = mixed_batch(num_seqs, total_q, max_query_len, dtype);
   DecodePlan plan = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                                max_context_len, dtype);
+                                max_context_len, dtype, 0, false, mixed);
   PrefillPlan pplan = plan_prefill(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, dtype, plan.ws_bytes);
   const size_t need = required_workspace(num_seqs, total_q, num_q_heads, num_kv_heads,
@@ -252,10 +271,18 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // bf16 rows of chunks (q_len >= 2) go to the MFMA kernel, all other rows to the
-  // decode kernel.  A single sequence with several rows has no decode row.
+  // decode kernel; a batch that may hold both runs them in one mixed launch, the slot
+  // write first (the chunk tiles read this step's rows from the pool).
   const bool chunks = dtype == PKV_BF16 && max_query_len > 1;
   const bool decode_rows = !(chunks && num_seqs == 1 && total_q > 1);
   hipError_t e = hipSuccess;
+  if (mixed) {
+    if (with_write)
+      e = launch_kv_write(k_new, v_new, const_cast<void *>(k_pool), const_cast<void *>(v_pool),
+                          slot_mapping, total_q, num_blocks, num_kv_heads, head_dim, dtype, st);
+    if (e == hipSuccess) e = launch_mixed(a, pplan, plan, st);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  }
   if (with_write) {
     if (dtype == PKV_BF16 && decode_rows) {
       // The bf16 decode kernel stores the new rows itself and reads each decode row's

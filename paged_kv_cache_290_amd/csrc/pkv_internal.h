@@ -93,9 +93,11 @@ struct DecodePlan {
   void *workspace;      // set by the caller before launching
 };
 
+// mixed: the decode rows run in the workgroups of the chunk launch that follow its
+// tiles (kDecodeWavesMin waves each).
 DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_heads,
                        int head_dim, int max_context_len, pkv_dtype dtype,
-                       int skip_blocks = 0, bool cascade = false);
+                       int skip_blocks = 0, bool cascade = false, bool mixed = false);
 
 struct AttnArgs {
   void *out;
@@ -137,6 +139,11 @@ hipError_t launch_kv_write(const void *k_new, const void *v_new, void *k_pool,
 
 hipError_t launch_decode(const AttnArgs &a, const DecodePlan &p, pkv_dtype dtype,
                          hipStream_t stream);
+// Kernel arguments of a decode plan, and the merge of its key ranges alone (for plans
+// whose decode workgroups ran inside another launch).
+SegArgs decode_seg_args(const DecodePlan &p, int num_kv_heads);
+hipError_t launch_decode_merge(const AttnArgs &a, const DecodePlan &p, pkv_dtype dtype,
+                               hipStream_t stream);
 
 // Prefill (chunk) plan.  A workgroup owns kPrefillCols (query row, q head) columns of
 // one KV head; with fewer tiles than compute units the key range of each tile is split
@@ -173,6 +180,15 @@ PrefillPlan plan_shared_run(int total_q, int num_q_heads, int num_kv_heads, int 
                             int shared_keys, size_t ws_offset);
 hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &p, pkv_dtype dtype,
                           hipStream_t stream);
+// A batch of chunks and decode rows (bf16) in one launch: the chunk tiles first, then
+// the decode workgroups of plan `dp` (planned with mixed = true), then the merges.
+hipError_t launch_mixed(const AttnArgs &a, const PrefillPlan &pp, const DecodePlan &dp,
+                        hipStream_t stream);
+// Decode head group that the mixed launch pairs with a chunk head group (equal to the
+// one plan_decode picks for the same GQA group).
+constexpr int mixed_decode_head_group(int head_dim, int chunk_head_group) {
+  return head_dim == 64 ? chunk_head_group : (chunk_head_group > 2 ? 2 : chunk_head_group);
+}
 // The shared-run pass (prefill kernel in shared-run mode; partials only).
 hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &p, int shared_keys,
                              hipStream_t stream);

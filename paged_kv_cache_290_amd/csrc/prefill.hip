@@ -38,6 +38,7 @@
 // softmax denominator sums those same rounded weights (dot2 with ones), accumulation
 // is fp32, output is bf16 (RNE).  A negative scale is folded into the
 // sign of q (exact in bf16) so the kernel works with |scale|.
+#include "decode_body.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -52,10 +53,6 @@ constexpr int kCols = kPrefillCols;  // columns per workgroup
 constexpr int kTblCache = 256;  // block-table entries cached in LDS (4,096 keys)
 constexpr float kSlack = 8.0f;  // log2 units
 constexpr uint32_t kBf16Ones = 0x3F803F80u;  // two bf16 1.0
-// v_perm_b32 selectors: low halves of (s1, s0) -> (s1.lo, s0.lo), high halves likewise
-// (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
-constexpr uint32_t kPermLo = 0x05040100u;
-constexpr uint32_t kPermHi = 0x07060302u;
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -293,11 +290,15 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
 
 }  // namespace
 
-template <int D, int HGP>
+// MIXED: the workgroups past the chunk's tiles each run one decode workgroup of plan
+// `dp` (kDecodeWavesMin = 8 waves, the decode kernel's body, its LDS laid over this
+// kernel's tiles), so the decode rows of a mixed batch fill the compute units that the
+// chunk's shorter row tiles leave idle.
+template <int D, int HGP, bool MIXED>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                                                                  int num_head_groups,
                                                                  int tile_slots,
-                                                                 PrefillSplit ps) {
+                                                                 PrefillSplit ps, SegArgs dp) {
   constexpr int BMQ = kCols / HGP;  // query rows per workgroup
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
@@ -331,7 +332,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int units = a.num_kv_heads * num_head_groups;
   const int total = tile_slots * units * ps.splits;
   const int u = blockIdx.x;
-  if (u >= total) return;
+  if (u >= total) {
+    if constexpr (MIXED) {
+      constexpr int HGD = mixed_decode_head_group(D, HGP);
+      using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
+      static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
+      static_assert(sizeof(DL) <= sizeof(lds), "the decode LDS must fit in the tiles");
+      decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(a, dp, (int64_t)(u - total),
+                                                        *reinterpret_cast<DL *>(lds));
+    }
+    return;
+  }
   const int split = u % ps.splits;
   const int tile = u / ps.splits;
   const int tid = threadIdx.x;
@@ -674,9 +685,18 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(AttnArgs a, PrefillS
 
 template <int D, int HGP>
 static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
-                                   hipStream_t st) {
+                                   hipStream_t st, const DecodePlan *dpl = nullptr) {
   const int total = pl.tiles * pl.splits;
-  if (total == 0) return hipSuccess;
+  int64_t dec_wgs = 0;
+  SegArgs dp{};
+  if (dpl) {
+    if (dpl->head_group != mixed_decode_head_group(D, HGP) || dpl->waves != kDecodeWavesMin)
+      return hipErrorInvalidValue;
+    dp = decode_seg_args(*dpl, a.num_kv_heads);
+    dec_wgs = (int64_t)dp.items * dp.groups * dp.splits;
+  }
+  if (total + dec_wgs > INT32_MAX) return hipErrorInvalidValue;
+  if (total + dec_wgs == 0) return hipSuccess;
   PrefillSplit ps{};
   ps.splits = pl.splits;
   ps.shared_keys = shared_keys;
@@ -686,9 +706,14 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
     ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
   }
-  prefill_mfma_kernel<D, HGP><<<dim3(total), dim3(kPThreads), 0, st>>>(a, pl.num_head_groups,
-                                                                        pl.tile_slots, ps);
+  if (dpl)
+    prefill_mfma_kernel<D, HGP, true><<<dim3((unsigned)(total + dec_wgs)), dim3(kPThreads), 0,
+                                        st>>>(a, pl.num_head_groups, pl.tile_slots, ps, dp);
+  else
+    prefill_mfma_kernel<D, HGP, false><<<dim3(total), dim3(kPThreads), 0, st>>>(
+        a, pl.num_head_groups, pl.tile_slots, ps, dp);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && dpl) e = launch_decode_merge(a, *dpl, PKV_BF16, st);
   // A shared run's partials are merged with the rows' other parts elsewhere.
   if (e != hipSuccess || pl.splits == 1 || shared_keys > 0) return e;
   prefill_merge_kernel<D><<<dim3(pl.tiles * (kCols * D / 4 / 256)), dim3(256), 0, st>>>(a, ps);
@@ -697,11 +722,11 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
 
 template <int D>
 static hipError_t launch_prefill_d(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
-                                   hipStream_t st) {
+                                   hipStream_t st, const DecodePlan *dpl = nullptr) {
   switch (pl.head_group) {
-    case 4: return launch_prefill_t<D, 4>(a, pl, shared_keys, st);
-    case 2: return launch_prefill_t<D, 2>(a, pl, shared_keys, st);
-    case 1: return launch_prefill_t<D, 1>(a, pl, shared_keys, st);
+    case 4: return launch_prefill_t<D, 4>(a, pl, shared_keys, st, dpl);
+    case 2: return launch_prefill_t<D, 2>(a, pl, shared_keys, st, dpl);
+    case 1: return launch_prefill_t<D, 1>(a, pl, shared_keys, st, dpl);
   }
   return hipErrorInvalidValue;
 }
@@ -711,6 +736,13 @@ hipError_t launch_prefill(const AttnArgs &a, const PrefillPlan &pl, pkv_dtype dt
   if (dtype != PKV_BF16) return hipErrorInvalidValue;
   if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, 0, stream);
   if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, 0, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mixed(const AttnArgs &a, const PrefillPlan &pp, const DecodePlan &dp,
+                        hipStream_t stream) {
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, pp, 0, stream, &dp);
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, pp, 0, stream, &dp);
   return hipErrorInvalidValue;
 }
 

@@ -102,7 +102,8 @@ def test_workspace_size_plan():
     """Decode rows need scratch only where a segment (row, kv-head group) is cut into
     several key ranges: when one range would give a wave more than 16 blocks, or when
     the segments alone cannot fill the GPU's 256 compute units (the answer without a
-    GPU).  Chunks add scratch where their tiles are split over the key range."""
+    GPU).  Chunks add scratch where their tiles are split over the key range; decode
+    rows that share a launch with chunks run in 8-wave workgroups."""
     lib = _lib.load()
     ws = lib.paged_attention_workspace_size
     # 32 x 8 segments of <= 128 blocks: one workgroup each, outputs written directly.
@@ -122,6 +123,12 @@ def test_workspace_size_plan():
     assert ws(1, 1, 2, 1, 64, 33001, _lib.PKV_F32) > 0
     # a chunk with few tiles over a long context: split partials
     assert ws(1, 40, 16, 8, 128, 6000, _lib.PKV_BF16) > 0
+    # several sequences with more rows than sequences (a chunk and decode rows): the
+    # decode rows run in the chunk launch's 8-wave workgroups, so rows past 2,048 keys
+    # are cut into key ranges; with as many rows as sequences the plain plan applies
+    assert ws(32, 2048, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
+    assert ws(32, 2048, 16, 8, 128, 4096, _lib.PKV_BF16) > 0
+    assert ws(32, 32, 16, 8, 128, 4096, _lib.PKV_BF16) == 0
     assert ws(0, 0, 32, 8, 64, 2048, _lib.PKV_BF16) == 0
     assert ws(4, 4, 6, 4, 64, 2048, _lib.PKV_BF16) == 0       # invalid heads
 
