@@ -38,6 +38,8 @@
 // softmax denominator sums those same rounded weights (dot2 with ones), accumulation
 // is fp32, output is bf16 (RNE).  A negative scale is folded into the
 // sign of q (exact in bf16) so the kernel works with |scale|.
+#include <algorithm>
+
 #include "decode_body.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -294,11 +296,16 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
 // `dp` (kDecodeWavesMin = 8 waves, the decode kernel's body, its LDS laid over this
 // kernel's tiles), so the decode rows of a mixed batch fill the compute units that the
 // chunk's shorter row tiles leave idle.
+// The workgroups of a mixed launch are, in order: the first `mix_first` chunk
+// workgroups (row tiles that surely exist), the `mix_dec` decode workgroups, then the
+// other chunk workgroups (slots that may be empty), so that the units freed by short
+// row tiles go to decode work rather than to empty slots.
 template <int D, int HGP, bool MIXED>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                                                                  int num_head_groups,
                                                                  int tile_slots,
-                                                                 PrefillSplit ps, SegArgs dp) {
+                                                                 PrefillSplit ps, SegArgs dp,
+                                                                 int mix_first, int mix_dec) {
   constexpr int BMQ = kCols / HGP;  // query rows per workgroup
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
@@ -331,18 +338,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   // engines and ran in two rounds, taking twice as long).
   const int units = a.num_kv_heads * num_head_groups;
   const int total = tile_slots * units * ps.splits;
-  const int u = blockIdx.x;
-  if (u >= total) {
-    if constexpr (MIXED) {
-      constexpr int HGD = mixed_decode_head_group(D, HGP);
-      using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
-      static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
-      static_assert(sizeof(DL) <= sizeof(lds), "the decode LDS must fit in the tiles");
-      decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(a, dp, (int64_t)(u - total),
-                                                        *reinterpret_cast<DL *>(lds));
+  int u = blockIdx.x;
+  if constexpr (MIXED) {
+    if (u >= mix_first) {
+      if (u < mix_first + mix_dec) {
+        constexpr int HGD = mixed_decode_head_group(D, HGP);
+        using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
+        static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
+        static_assert(sizeof(DL) <= sizeof(lds), "the decode LDS must fit in the tiles");
+        decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(a, dp, (int64_t)(u - mix_first),
+                                                          *reinterpret_cast<DL *>(lds));
+        return;
+      }
+      u -= mix_dec;
     }
-    return;
   }
+  if (u >= total) return;
   const int split = u % ps.splits;
   const int tile = u / ps.splits;
   const int tid = threadIdx.x;
@@ -688,12 +699,23 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
                                    hipStream_t st, const DecodePlan *dpl = nullptr) {
   const int total = pl.tiles * pl.splits;
   int64_t dec_wgs = 0;
+  int first = total;
   SegArgs dp{};
   if (dpl) {
     if (dpl->head_group != mixed_decode_head_group(D, HGP) || dpl->waves != kDecodeWavesMin)
       return hipErrorInvalidValue;
     dp = decode_seg_args(*dpl, a.num_kv_heads);
-    dec_wgs = (int64_t)dp.items * dp.groups * dp.splits;
+    // Padded to a multiple of the XCD count, so that the chunk workgroups after the
+    // decode ones keep their XCD (workgroups go to XCDs round-robin by index).
+    dec_wgs = ((int64_t)dp.items * dp.groups * dp.splits + 7) / 8 * 8;
+    // Row tiles that surely exist: the chunk sequences hold at least total_q -
+    // (num_seqs - 1) rows (every other sequence has at most one), so the batch has at
+    // least ceil((total_q - num_seqs + 1) / BM) row tiles.
+    const int bm = kCols / HGP;
+    const int sure = std::max(0, (a.total_q - a.num_seqs + 1 + bm - 1) / bm);
+    first = (int)std::min<int64_t>(total, (int64_t)std::min(sure, pl.tile_slots) *
+                                               a.num_kv_heads * pl.num_head_groups *
+                                               pl.splits);
   }
   if (total + dec_wgs > INT32_MAX) return hipErrorInvalidValue;
   if (total + dec_wgs == 0) return hipSuccess;
@@ -708,10 +730,11 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
   }
   if (dpl)
     prefill_mfma_kernel<D, HGP, true><<<dim3((unsigned)(total + dec_wgs)), dim3(kPThreads), 0,
-                                        st>>>(a, pl.num_head_groups, pl.tile_slots, ps, dp);
+                                        st>>>(a, pl.num_head_groups, pl.tile_slots, ps, dp,
+                                              first, (int)dec_wgs);
   else
     prefill_mfma_kernel<D, HGP, false><<<dim3(total), dim3(kPThreads), 0, st>>>(
-        a, pl.num_head_groups, pl.tile_slots, ps, dp);
+        a, pl.num_head_groups, pl.tile_slots, ps, dp, total, 0);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && dpl) e = launch_decode_merge(a, *dpl, PKV_BF16, st);
   // A shared run's partials are merged with the rows' other parts elsewhere.
