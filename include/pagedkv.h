@@ -155,14 +155,16 @@ pkv_status paged_attention_varlen(void *out, const void *q, const void *k_pool,
  * same arguments, under one extra precondition: new row t (a query row, [total_q]) is
  * the token at position context_len - q_len + i of its sequence (i its index among the
  * sequence's rows), and slot_mapping[t] is that position's table slot
- * (block_tables[s][pos / 16] * 16 + pos % 16).  With that, bf16 single-token rows
- * read their newest key and value straight from k_new / v_new while the same kernel
- * stores all new rows, saving the separate write launch.  Other cases run the write
- * kernel first; so do bf16 batches of several sequences with more query rows than
- * sequences, whose chunk tiles and decode rows then share one attention launch (the
- * decode rows in the workgroups after the chunk tiles, filling the compute units that
- * the chunk's shorter row tiles free).  Arguments as for the two calls above (k_new,
- * v_new [total_q][Hkv][D]).
+ * (block_tables[s][pos / 16] * 16 + pos % 16).  With that, the first bf16 attention
+ * launch stores all new rows itself and reads this step's keys and values straight
+ * from k_new / v_new, saving the separate write launch: the decode kernel (decode
+ * rows read their newest key and value there) and, for a batch of one chunk sequence,
+ * the chunk kernel (its tiles read every new position there).  Other cases run the
+ * write kernel first: fp32, and bf16 batches of several sequences with more query rows
+ * than sequences, whose chunk tiles and decode rows then share one attention launch
+ * (the decode rows in the workgroups after the chunk tiles, filling the compute units
+ * that the chunk's shorter row tiles free).  Arguments as for the two calls above
+ * (k_new, v_new [total_q][Hkv][D]).
  */
 pkv_status paged_attention_varlen_with_write(
     void *out, const void *q, const void *k_new, const void *v_new, void *k_pool,

@@ -276,17 +276,13 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
   const bool chunks = dtype == PKV_BF16 && max_query_len > 1;
   const bool decode_rows = !(chunks && num_seqs == 1 && total_q > 1);
   hipError_t e = hipSuccess;
-  if (mixed) {
-    if (with_write)
-      e = launch_kv_write(k_new, v_new, const_cast<void *>(k_pool), const_cast<void *>(v_pool),
-                          slot_mapping, total_q, num_blocks, num_kv_heads, head_dim, dtype, st);
-    if (e == hipSuccess) e = launch_mixed(a, pplan, plan, st);
-    return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
-  }
   if (with_write) {
-    if (dtype == PKV_BF16 && decode_rows) {
-      // The bf16 decode kernel stores the new rows itself and reads each decode row's
-      // newest key/value from k_new / v_new; the chunk kernel runs after it.
+    if (dtype == PKV_BF16 && !mixed) {
+      // The first bf16 attention launch (the decode kernel, or the chunk kernel of a
+      // single sequence) stores the new rows itself and reads this step's keys and
+      // values from k_new / v_new (the fused-call precondition places new row i of a
+      // sequence at position context_len - q_len + i).  A mixed launch reads them from
+      // the pools, written first.
       a.k_new = k_new;
       a.v_new = v_new;
       a.slot_mapping = slot_mapping;
@@ -296,8 +292,20 @@ pkv_status attention_impl(void *out, const void *q, const void *k_new, const voi
                           num_kv_heads, head_dim, dtype, st);
     }
   }
+  if (mixed) {
+    if (e == hipSuccess) e = launch_mixed(a, pplan, plan, st);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  }
   if (e == hipSuccess && decode_rows) e = launch_decode(a, plan, dtype, st);
-  if (e == hipSuccess && chunks) e = launch_prefill(a, pplan, dtype, st);
+  if (e == hipSuccess && chunks) {
+    AttnArgs ac = a;
+    if (decode_rows) {  // the decode launch has stored the new rows
+      ac.k_new = nullptr;
+      ac.v_new = nullptr;
+      ac.slot_mapping = nullptr;
+    }
+    e = launch_prefill(ac, pplan, dtype, st);
+  }
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -48,30 +48,9 @@ __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<T>(), decode_waves_per_simd<T>())))
 void decode_kernel(AttnArgs a, SegArgs p) {
   __shared__ DecodeLds<T, D, HG, NW> sh;
-  if (a.k_new != nullptr) {
-    // Fused slot write of every new row (16-byte pieces spread over the grid).  No
-    // workgroup reads those slots from the pool: each decode row's newest key and
-    // value come from k_new / v_new below, and chunk rows run in a later launch.
-    constexpr int kRowVecs = D * (int)sizeof(T) / 16;
-    const int64_t total = (int64_t)a.total_q * a.num_kv_heads * kRowVecs;
-    const int64_t per_token = (int64_t)a.num_kv_heads * kRowVecs;
-    const int64_t num_slots = (int64_t)a.num_blocks * kBlock;
-    for (int64_t idx = (int64_t)blockIdx.x * (64 * NW) + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * (64 * NW)) {
-      const int64_t t = idx / per_token;
-      const int rem = (int)(idx - t * per_token);
-      const int h = rem / kRowVecs;
-      const int piece = rem - h * kRowVecs;
-      const uint4 kx = static_cast<const uint4 *>(a.k_new)[idx];
-      const uint4 vx = static_cast<const uint4 *>(a.v_new)[idx];
-      const int64_t slot = a.slot_mapping[t];
-      if (slot < 0 || slot >= num_slots) continue;
-      const int64_t dst = ((slot / kBlock * a.num_kv_heads + h) * kBlock + slot % kBlock) *
-                              kRowVecs + piece;
-      static_cast<uint4 *>(const_cast<void *>(a.k_pool))[dst] = kx;
-      static_cast<uint4 *>(const_cast<void *>(a.v_pool))[dst] = vx;
-    }
-  }
+  // Fused call: the launch stores every new row; each decode row's newest key and
+  // value come from k_new / v_new.
+  if (a.k_new != nullptr) fused_slot_write<T, D>(a, blockIdx.x, gridDim.x, 64 * NW);
 
   // Virtual order (g, item, split): the workgroups of one kv-head group sit on one
   // XCD, sharing its L2 for shared blocks.

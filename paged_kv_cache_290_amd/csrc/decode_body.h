@@ -123,6 +123,34 @@ constexpr int decode_waves_per_simd() {
   return std::is_same<T, float>::value ? 2 : 4;
 }
 
+// Fused slot write: every new row's key and value (D elements of T per kv head) stored
+// at its slot, in 16-byte pieces spread over the workgroups of the calling launch
+// (workgroup wg of nwg, nthr threads each).  Slots outside the pool are skipped.  The
+// launch reads none of these slots from the pool: the attention work of the same
+// launch takes this step's keys and values from k_new / v_new.
+template <typename T, int D>
+__device__ __forceinline__ void fused_slot_write(const AttnArgs &a, int64_t wg, int64_t nwg,
+                                                 int nthr) {
+  constexpr int kRowVecs = D * (int)sizeof(T) / 16;
+  const int64_t total = (int64_t)a.total_q * a.num_kv_heads * kRowVecs;
+  const int64_t per_token = (int64_t)a.num_kv_heads * kRowVecs;
+  const int64_t num_slots = (int64_t)a.num_blocks * kBlock;
+  for (int64_t idx = wg * nthr + threadIdx.x; idx < total; idx += nwg * nthr) {
+    const int64_t t = idx / per_token;
+    const int rem = (int)(idx - t * per_token);
+    const int h = rem / kRowVecs;
+    const int piece = rem - h * kRowVecs;
+    const uint4 kx = static_cast<const uint4 *>(a.k_new)[idx];
+    const uint4 vx = static_cast<const uint4 *>(a.v_new)[idx];
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t dst =
+        ((slot / kBlock * a.num_kv_heads + h) * kBlock + slot % kBlock) * kRowVecs + piece;
+    static_cast<uint4 *>(const_cast<void *>(a.k_pool))[dst] = kx;
+    static_cast<uint4 *>(const_cast<void *>(a.v_pool))[dst] = vx;
+  }
+}
+
 // LDS of one decode workgroup of NW waves.  bf16 dot-product path: per wave and ring
 // slot, partial scores [j*HG + hh][lane] and the bf16 weights [token group][head][j]
 // exchanged between the lanes of the wave; matrix-core path: each wave's current V

@@ -39,6 +39,7 @@
 // is fp32, output is bf16 (RNE).  A negative scale is folded into the
 // sign of q (exact in bf16) so the kernel works with |scale|.
 #include <algorithm>
+#include <climits>
 
 #include "decode_body.h"
 #include "pkv_device.h"
@@ -299,8 +300,10 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
 // The workgroups of a mixed launch are, in order: the first `mix_first` chunk
 // workgroups (row tiles that surely exist), the `mix_dec` decode workgroups, then the
 // other chunk workgroups (slots that may be empty), so that the units freed by short
-// row tiles go to decode work rather than to empty slots.
-template <int D, int HGP, bool MIXED>
+// row tiles go to decode work rather than to empty slots.  Without decode workgroups
+// mix_dec is 0 and mix_first the number of row-tile workgroups that surely exist (at
+// least one).
+template <int D, int HGP, bool MIXED, bool FUSED>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                                                                  int num_head_groups,
                                                                  int tile_slots,
@@ -339,6 +342,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int units = a.num_kv_heads * num_head_groups;
   const int total = tile_slots * units * ps.splits;
   int u = blockIdx.x;
+  // FUSED (the chunk launch of a fused call with one sequence): the launch stores this
+  // step's new rows, the first mix_first workgroups a share each (those dispatched
+  // first: the row tiles that surely exist), and the chunk tiles read those keys and
+  // values from k_new / v_new.
+  if constexpr (FUSED) {
+    if ((int)blockIdx.x < mix_first)
+      fused_slot_write<uint16_t, D>(a, blockIdx.x, mix_first, kPThreads);
+  }
   if constexpr (MIXED) {
     if (u >= mix_first) {
       if (u < mix_first + mix_dec) {
@@ -496,18 +507,45 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                      (kch ^ swz_k<D>(kkey0)) * 16;
   const char *vthr = reinterpret_cast<const char *>(vpool) + row_off +
                      (kch ^ swz_v<D>(kkey0)) * 16;
-#define PKV_FETCH(st, buf)                                                               \
-  do {                                                                                   \
-    const int b0_ = ((st) * (kStepKeys / kBlock)) % kTblCache;                           \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                    \
-      const uint64_t off_ =                                                              \
-          (uint64_t)(uint32_t)s_tbl[b0_ + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;   \
-      const int key_ = kw0 + KSTRIDE * i;                                                \
-      const int row_ = ((buf) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH; \
-      load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));                      \
-      load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));                      \
-    }                                                                                    \
-  } while (0)
+  // Fused call: this step's rows (positions new0 = ctx - q_len onward) are read from
+  // k_new / v_new, position p at row q_begin + p - new0, since this launch is still
+  // writing their slots.  Otherwise new0 lies past every key.
+  const bool new_rows = FUSED && !shared;
+  const int new0 = new_rows ? ctx - q_len : INT_MAX;
+  const size_t nrow_bytes = (size_t)a.num_kv_heads * D * 2;
+  const size_t nrow_off = (size_t)kvh * D * 2;
+  const char *knthr = new_rows ? static_cast<const char *>(a.k_new) + nrow_off +
+                                     (kch ^ swz_k<D>(kkey0)) * 16
+                               : nullptr;
+  const char *vnthr = new_rows ? static_cast<const char *>(a.v_new) + nrow_off +
+                                     (kch ^ swz_v<D>(kkey0)) * 16
+                               : nullptr;
+  // Part i of the staging of step s into buffer b.  Fused call: a step that holds new
+  // positions (uniform over the workgroup) reads those from k_new / v_new; positions
+  // past the sequence's last row (masked keys of the last step) read that row.
+  auto fetch = [&](int s, int b, int i) {
+    const int k0 = s * kStepKeys;
+    const int key_ = kw0 + KSTRIDE * i;
+    const int row_ = (b * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH;
+    const uint64_t off_ =
+        (uint64_t)(uint32_t)s_tbl[(s * (kStepKeys / kBlock)) % kTblCache +
+                                  (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;
+    const char *ks = kthr + off_;
+    const char *vs = vthr + off_;
+    if constexpr (FUSED) {
+      if (k0 + kStepKeys > new0) {
+        const int pos = k0 + kkey0 + KSTRIDE * i;
+        const int r = min(max(pos, new0), ctx - 1) - new0;
+        const size_t noff = (size_t)(q_begin + r) * nrow_bytes;
+        if (pos >= new0) {
+          ks = knthr + noff;
+          vs = vnthr + noff;
+        }
+      }
+    }
+    load_lds16(ks, (uint32_t)(uintptr_t)(k_lds + row_));
+    load_lds16(vs, (uint32_t)(uintptr_t)(v_lds + row_));
+  };
   // After this wave's loads of step st have completed: zero its V slots past kv_end
   // (only the last step has any).
 #define PKV_ZERO_TAIL(st, buf)                                                           \
@@ -533,7 +571,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
             col_row[cg] * a.num_q_heads + col_head[cg];
   }
   if (st0 < nst) {
-    PKV_FETCH(st0, st0 & 1);
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) fetch(st0, st0 & 1, i);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed in LDS
     PKV_ZERO_TAIL(st0, st0 & 1);
   }
@@ -558,15 +597,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
     // block 0), so those loads read valid pool rows into the buffer no step reads any
     // more, and they have landed before the barrier that ends the loop.
     static_assert(KCH == KS, "one staging part per k-step");
-    const int fb0 = ((st + 1) * (kStepKeys / kBlock)) % kTblCache;
-    auto fetch_part = [&](int i) {
-      const uint64_t off_ =
-          (uint64_t)(uint32_t)s_tbl[fb0 + (kkey0 + KSTRIDE * i) / kBlock] * blk_bytes;
-      const int key_ = kw0 + KSTRIDE * i;
-      const int row_ = ((buf ^ 1) * 2 + key_ / kHalfKeys) * K_U4 + (key_ % kHalfKeys) * NCH;
-      load_lds16(kthr + off_, (uint32_t)(uintptr_t)(k_lds + row_));
-      load_lds16(vthr + off_, (uint32_t)(uintptr_t)(v_lds + row_));
-    };
+    auto fetch_part = [&](int i) { fetch(st + 1, buf ^ 1, i); };
 
     const int kbase = st * kStepKeys + half * kHalfKeys;
     if (kbase < kv_end) {
@@ -652,7 +683,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
 }
 
 #undef PKV_FILL_TBL
-#undef PKV_FETCH
 #undef PKV_ZERO_TAIL
 
 // Log-sum-exp merge of the splits of each tile column: out = sum_s 2^(lse_s - M) o_s /
@@ -699,7 +729,6 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
                                    hipStream_t st, const DecodePlan *dpl = nullptr) {
   const int total = pl.tiles * pl.splits;
   int64_t dec_wgs = 0;
-  int first = total;
   SegArgs dp{};
   if (dpl) {
     if (dpl->head_group != mixed_decode_head_group(D, HGP) || dpl->waves != kDecodeWavesMin)
@@ -708,15 +737,15 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     // Padded to a multiple of the XCD count, so that the chunk workgroups after the
     // decode ones keep their XCD (workgroups go to XCDs round-robin by index).
     dec_wgs = ((int64_t)dp.items * dp.groups * dp.splits + 7) / 8 * 8;
-    // Row tiles that surely exist: the chunk sequences hold at least total_q -
-    // (num_seqs - 1) rows (every other sequence has at most one), so the batch has at
-    // least ceil((total_q - num_seqs + 1) / BM) row tiles.
-    const int bm = kCols / HGP;
-    const int sure = std::max(0, (a.total_q - a.num_seqs + 1 + bm - 1) / bm);
-    first = (int)std::min<int64_t>(total, (int64_t)std::min(sure, pl.tile_slots) *
-                                               a.num_kv_heads * pl.num_head_groups *
-                                               pl.splits);
   }
+  // Row tiles that surely exist: the chunk sequences hold at least total_q -
+  // (num_seqs - 1) rows (every other sequence has at most one), so the batch has at
+  // least ceil((total_q - num_seqs + 1) / BM) row tiles (a shared run: all its rows).
+  const int bm = kCols / HGP;
+  const int sure = std::max(1, (a.total_q - a.num_seqs + 1 + bm - 1) / bm);
+  const int first = (int)std::min<int64_t>(
+      total, (int64_t)std::min(sure, pl.tile_slots) * a.num_kv_heads * pl.num_head_groups *
+                 pl.splits);
   if (total + dec_wgs > INT32_MAX) return hipErrorInvalidValue;
   if (total + dec_wgs == 0) return hipSuccess;
   PrefillSplit ps{};
@@ -728,13 +757,24 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
     ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
   }
+  // Fused calls (k_new given) store the new rows in this launch; the shared-run pass
+  // of a shared prefix never does (its decode launch stores them).
+  const bool fused = a.k_new != nullptr && shared_keys == 0;
+  const dim3 grid((unsigned)(total + dec_wgs)), block(kPThreads);
+  const int nhg = pl.num_head_groups, slots = pl.tile_slots, ndec = (int)dec_wgs;
+  // A mixed launch reads the new rows from the pools (the caller writes them first):
+  // with k_new in a mixed launch, the chunk steps that read k_new and the stores of
+  // the new rows cost more than the separate write launch they save.
+  if (dpl && fused) return hipErrorInvalidValue;
   if (dpl)
-    prefill_mfma_kernel<D, HGP, true><<<dim3((unsigned)(total + dec_wgs)), dim3(kPThreads), 0,
-                                        st>>>(a, pl.num_head_groups, pl.tile_slots, ps, dp,
-                                              first, (int)dec_wgs);
+    prefill_mfma_kernel<D, HGP, true, false><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
+                                                                     first, ndec);
+  else if (fused)
+    prefill_mfma_kernel<D, HGP, false, true><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
+                                                                     first, 0);
   else
-    prefill_mfma_kernel<D, HGP, false><<<dim3(total), dim3(kPThreads), 0, st>>>(
-        a, pl.num_head_groups, pl.tile_slots, ps, dp, total, 0);
+    prefill_mfma_kernel<D, HGP, false, false><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
+                                                                      first, 0);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && dpl) e = launch_decode_merge(a, *dpl, PKV_BF16, st);
   // A shared run's partials are merged with the rows' other parts elsewhere.
