@@ -47,7 +47,13 @@ template <typename T, int D, int HG, int NW>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<T>(), decode_waves_per_simd<T>())))
 void decode_kernel(AttnArgs a, SegArgs p) {
-  __shared__ DecodeLds<T, D, HG, NW> sh;
+  using L = DecodeLds<T, D, HG, NW>;
+  __shared__ typename L::Red s_red;
+  __shared__ typename L::Pw s_pw;
+  __shared__ typename L::V s_v;
+  __shared__ typename L::O s_o;
+  __shared__ typename L::Ml s_ml;
+  const L sh{s_red, s_pw, s_v, s_o, s_ml};
   // Fused call: the launch stores every new row; each decode row's newest key and
   // value come from k_new / v_new.
   if (a.k_new != nullptr) fused_slot_write<T, D>(a, blockIdx.x, gridDim.x, 64 * NW);

@@ -155,7 +155,8 @@ __device__ __forceinline__ void fused_slot_write(const AttnArgs &a, int64_t wg, 
 // slot, partial scores [j*HG + hh][lane] and the bf16 weights [token group][head][j]
 // exchanged between the lanes of the wave; matrix-core path: each wave's current V
 // tile (rows permuted by vslot); both: the waves' states for the merge (unnormalised
-// outputs, reference max, weight sum).
+// outputs, reference max, weight sum).  The decode kernel declares the five arrays as
+// __shared__ arrays of its own; the mixed launch lays them over its tile buffers.
 template <typename T, int D, int HG, int NW>
 struct DecodeLds {
   using M = DecodeMap<T, D>;
@@ -165,18 +166,39 @@ struct DecodeLds {
   static constexpr int kTileBytes = kBlock * D * (int)sizeof(T);
   static constexpr int kRed = (kF32 || kMfma) ? 1 : M::NV * HG * 64;
   static constexpr int kPw = (kF32 || kMfma) ? 1 : 16 * HG / 2;
-  float red[NW][PF + 1][kRed];
-  uint32_t pw[NW][PF + 1][kPw];
-  uint4 v[kMfma ? NW * kTileBytes / 16 : 1];
-  float o[NW][HG][D];
-  float ml[NW][HG][2];
+  static constexpr int kV = kMfma ? NW * kTileBytes / 16 : 1;
+  typedef float Red[NW][PF + 1][kRed];
+  typedef uint32_t Pw[NW][PF + 1][kPw];
+  typedef uint4 V[kV];
+  typedef float O[NW][HG][D];
+  typedef float Ml[NW][HG][2];
+  Red &red;
+  Pw &pw;
+  V &v;
+  O &o;
+  Ml &ml;
+  // Bytes of the five arrays laid out one after another (16-byte aligned each).
+  static constexpr size_t bytes() {
+    return al(sizeof(Red)) + al(sizeof(Pw)) + al(sizeof(V)) + al(sizeof(O)) + al(sizeof(Ml));
+  }
+  // The arrays laid out from `base` (16-byte aligned LDS of at least bytes()).
+  static __device__ DecodeLds over(char *base) {
+    char *p = base;
+    Red &r = *reinterpret_cast<Red *>(p); p += al(sizeof(Red));
+    Pw &w = *reinterpret_cast<Pw *>(p); p += al(sizeof(Pw));
+    V &vv = *reinterpret_cast<V *>(p); p += al(sizeof(V));
+    O &oo = *reinterpret_cast<O *>(p); p += al(sizeof(O));
+    Ml &m = *reinterpret_cast<Ml *>(p);
+    return DecodeLds{r, w, vv, oo, m};
+  }
+  static constexpr size_t al(size_t n) { return (n + 15) / 16 * 16; }
 };
 
 // The work of decode workgroup v (a segment's key range) by the calling workgroup of
 // NW waves, with its LDS in `sh`.
 template <typename T, int D, int HG, int NW>
 __device__ __forceinline__ void decode_segment(AttnArgs a, SegArgs p, int64_t v,
-                                               DecodeLds<T, D, HG, NW> &sh) {
+                                               DecodeLds<T, D, HG, NW> sh) {
   constexpr bool kF32 = std::is_same<T, float>::value;
   using M = DecodeMap<T, D>;
   constexpr int CPR = M::CPR, TPI = M::TPI, NV = M::NV, EPC = M::EPC, WPC = M::WPC;
@@ -678,11 +700,14 @@ __device__ __forceinline__ void decode_segment(AttnArgs a, SegArgs p, int64_t v,
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[hh][e] = sum_over_chunk_lanes<CPR>(acc[hh][e]);
     }
+    // Lanes < CPR hold chunk `lane` (indexing by lane rather than the chunk index
+    // computed before the loop keeps that index from staying live across it: at 128
+    // registers it was spilled).
     if (lane < CPR) {
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s_o[wave][hh][chunk * EPC + e] = acc[hh][e];
+        for (int e = 0; e < EPC; ++e) s_o[wave][hh][lane * EPC + e] = acc[hh][e];
     }
     if (lane == 0) {
 #pragma unroll

@@ -356,9 +356,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         constexpr int HGD = mixed_decode_head_group(D, HGP);
         using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
         static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
-        static_assert(sizeof(DL) <= sizeof(lds), "the decode LDS must fit in the tiles");
-        decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(a, dp, (int64_t)(u - mix_first),
-                                                          *reinterpret_cast<DL *>(lds));
+        static_assert(DL::bytes() <= sizeof(lds), "the decode LDS must fit in the tiles");
+        decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(
+            a, dp, (int64_t)(u - mix_first), DL::over(reinterpret_cast<char *>(lds)));
         return;
       }
       u -= mix_dec;
