@@ -50,6 +50,7 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
   p.num_head_groups = p.group / p.head_group;
   p.items = dtype == PKV_F32 ? total_q : num_seqs;
   p.skip_blocks = skip_blocks;
+  p.max_context_len = max_context_len;
   p.cascade = cascade;
   // Workgroup size: bf16 waves hold 128 registers (four per SIMD), so a compute unit
   // runs one 16-wave or two 8-wave workgroups.  16 waves per segment while the

@@ -87,6 +87,7 @@ struct DecodePlan {
   int waves;            // waves per workgroup (kDecodeWavesMax or kDecodeWavesMin)
   int splits;           // key ranges (workgroups) per segment
   int skip_blocks;      // leading blocks of every row left out (a shared prefix), or 0
+  int max_context_len;  // the call's bound on context_lens
   bool cascade;         // partials even with one range, no merge launch (the shared-
                         // prefix merge combines them with the shared run's partials)
   size_t ws_o_offset, ws_lse_offset, ws_bytes;

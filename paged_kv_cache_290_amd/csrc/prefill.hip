@@ -97,29 +97,24 @@ __device__ __forceinline__ int swz_v(int row) {
   else return (row & 2) | (((row ^ (row >> 2)) & 1) << 2);
 }
 
-// Row tiles of a batch: a sequence with q_len >= 2 query rows (q_len <= total_q) has
-// ceil(q_len / BM) of them, numbered over the sequences in order; decode rows and
-// broken lengths have none.  Finds the sequence of row tile j and j's index among that
-// sequence's tiles (seq = -1 when j is past the last one).  Every thread of the
-// workgroup calls it (two barriers): thread t counts the tiles of a run of
-// ceil(num_seqs / threads) consecutive sequences, an exclusive scan over the threads
-// finds the run holding j, and that thread walks it.
-template <int BM>
-__device__ __forceinline__ void find_row_tile(const int32_t *qsl, int num_seqs, int total_q,
-                                              int j, int *s_find, int &seq, int &local) {
+// Item and index of element j of a sequence of n items in which item i holds count(i)
+// elements, numbered over the items in order (item = -1 when j is past the last
+// element).  Every thread of the workgroup calls it (two barriers): thread t counts the
+// elements of a run of ceil(n / threads) consecutive items, an exclusive scan over the
+// threads finds the run holding j, and that thread walks it.  s_find holds at least
+// waves + 2 ints.
+template <typename CF>
+__device__ __forceinline__ void find_in_runs(int n, int j, CF &&count, int *s_find,
+                                             int &item, int &local) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   constexpr int kW = kPThreads / 64;
-  auto tiles_of = [&](int s) {
-    const int q = qsl[s + 1] - qsl[s];
-    return (q >= 2 && q <= total_q) ? (q + BM - 1) / BM : 0;
-  };
-  const int per = (num_seqs + kPThreads - 1) / kPThreads;
-  const int s0 = min(tid * per, num_seqs);
-  const int s1 = min(s0 + per, num_seqs);
+  const int per = (n + kPThreads - 1) / kPThreads;
+  const int s0 = min(tid * per, n);
+  const int s1 = min(s0 + per, n);
   int cnt = 0;
-  for (int s = s0; s < s1; ++s) cnt += tiles_of(s);
+  for (int s = s0; s < s1; ++s) cnt += count(s);
   int inc = cnt;  // inclusive prefix over the wave's lanes
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -134,18 +129,72 @@ __device__ __forceinline__ void find_row_tile(const int32_t *qsl, int num_seqs, 
   if (j >= excl && j < excl + cnt) {
     int r = j - excl;
     for (int s = s0; s < s1; ++s) {
-      const int n = tiles_of(s);
-      if (r < n) {
+      const int c = count(s);
+      if (r < c) {
         s_find[kW] = s;
         s_find[kW + 1] = r;
         break;
       }
-      r -= n;
+      r -= c;
     }
   }
   __syncthreads();
-  seq = s_find[kW];
+  item = s_find[kW];
   local = s_find[kW + 1];
+}
+
+// Row tiles of a batch: a sequence with q_len >= 2 query rows (q_len <= total_q) has
+// ceil(q_len / BM) of them, numbered over the sequences in order; decode rows and
+// broken lengths have none.  Finds the sequence of row tile j and j's index among that
+// sequence's tiles (seq = -1 when j is past the last one).
+template <int BM>
+__device__ __forceinline__ void find_row_tile(const int32_t *qsl, int num_seqs, int total_q,
+                                              int j, int *s_find, int &seq, int &local) {
+  auto tiles_of = [&](int s) {
+    const int q = qsl[s + 1] - qsl[s];
+    return (q >= 2 && q <= total_q) ? (q + BM - 1) / BM : 0;
+  };
+  find_in_runs(num_seqs, j, tiles_of, s_find, seq, local);
+}
+
+// Decode workgroup k of a mixed launch -> the virtual workgroup of the decode plan it
+// runs, rows longest first (the workgroups are dispatched in order, so long pieces start
+// while the chunk's shorter row tiles end, and short ones fill the end).  All pieces
+// of a row are equally long (its key ranges are equal fractions), so workgroup k takes
+// piece k % (groups * splits) of the row of rank k / (groups * splits) in descending
+// context length; rows that are no decode row (the chunks, whose pieces do nothing)
+// come last.  The rank comes from a counting sort on buckets of `bucket_keys` keys
+// (rows of one bucket in index order) that every decode workgroup computes on its own:
+// a histogram of the 256 buckets, a scan of it, and a pass over the rows of the
+// bucket that holds the rank.  Returns a value past the plan's workgroups for padding
+// workgroups.  s_hist holds 256 ints, s_find at least waves + 2.
+__device__ __forceinline__ int64_t mixed_decode_piece(const AttnArgs &a, const SegArgs &dp, int k,
+                                                      int bucket_keys, int *s_hist,
+                                                      int *s_find) {
+  const int tid = threadIdx.x;
+  const int per_row = dp.groups * dp.splits;
+  const int r = k / per_row;
+  const int rem = k - r * per_row;
+  if (r >= dp.items) return (int64_t)dp.items * per_row;  // padding
+  auto bucket = [&](int i) {
+    const int q = a.query_start_loc[i + 1] - a.query_start_loc[i];
+    if (q != 1) return 255;
+    return 254 - min(253, max(a.context_lens[i], 0) / bucket_keys);
+  };
+  if (tid < 256) s_hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < dp.items; i += kPThreads) atomicAdd(&s_hist[bucket(i)], 1);
+  __syncthreads();
+  int b = -1, off = 0;
+  find_in_runs(256, r, [&](int x) { return s_hist[x]; }, s_find, b, off);
+  __syncthreads();  // every thread has read the result before s_find is reused
+  int row = -1, idx = 0;
+  find_in_runs(dp.items, off, [&](int i) { return bucket(i) == b ? 1 : 0; }, s_find, row,
+               idx);
+  if (row < 0) return (int64_t)dp.items * per_row;
+  const int g = rem / dp.splits;
+  const int split = rem - g * dp.splits;
+  return ((int64_t)g * dp.items + row) * dp.splits + split;
 }
 
 // One wave's update with a 64-key tile: kb and vb = K and V tiles, each row-major
@@ -300,7 +349,8 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
 // The workgroups of a mixed launch are, in order: the first `mix_first` chunk
 // workgroups (row tiles that surely exist), the `mix_dec` decode workgroups, then the
 // other chunk workgroups (slots that may be empty), so that the units freed by short
-// row tiles go to decode work rather than to empty slots.  Without decode workgroups
+// row tiles go to decode work rather than to empty slots; mix_bucket is the bucket
+// width (keys) of the decode rows' longest-first order.  Without decode workgroups
 // mix_dec is 0 and mix_first the number of row-tile workgroups that surely exist (at
 // least one).
 template <int D, int HGP, bool MIXED, bool FUSED>
@@ -308,7 +358,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
                                                                  int num_head_groups,
                                                                  int tile_slots,
                                                                  PrefillSplit ps, SegArgs dp,
-                                                                 int mix_first, int mix_dec) {
+                                                                 int mix_first, int mix_dec,
+                                                                 int mix_bucket) {
   constexpr int BMQ = kCols / HGP;  // query rows per workgroup
   constexpr int KS = D / 32;        // k-steps of S^T over head_dim
   constexpr int MT = D / 16;        // 16-dim row tiles of O^T
@@ -320,7 +371,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   static_assert(4 * XF * 64 * 4 <= LDS_U4 * 16, "merge exchange must fit the tiles");
   __shared__ uint4 lds[LDS_U4];
   __shared__ int s_tbl[kTblCache];  // block-table entries of this workgroup
-  __shared__ int s_find[kPThreads / 64 + 2];  // row-tile lookup
+  __shared__ int s_find[kPThreads / 64 + 2];  // row-tile and decode-order lookups
   uint4 *const k_lds = lds;             // [buf*2+half][K_U4]
   uint4 *const v_lds = lds + 4 * K_U4;  // [buf*2+half][K_U4]
 
@@ -357,8 +408,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
         static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
         static_assert(DL::bytes() <= sizeof(lds), "the decode LDS must fit in the tiles");
+        const int64_t v =
+            mixed_decode_piece(a, dp, u - mix_first, mix_bucket, s_tbl, s_find);
         decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(
-            a, dp, (int64_t)(u - mix_first), DL::over(reinterpret_cast<char *>(lds)));
+            a, dp, v, DL::over(reinterpret_cast<char *>(lds)));
         return;
       }
       u -= mix_dec;
@@ -766,15 +819,18 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
   // with k_new in a mixed launch, the chunk steps that read k_new and the stores of
   // the new rows cost more than the separate write launch they save.
   if (dpl && fused) return hipErrorInvalidValue;
+  // Buckets of the decode rows' longest-first order: 254 of them over the longest
+  // context (a longer row falls in the first).
+  const int bucket = std::max(1, (dpl ? dpl->max_context_len : 0) / 254 + 1);
   if (dpl)
     prefill_mfma_kernel<D, HGP, true, false><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
-                                                                     first, ndec);
+                                                                     first, ndec, bucket);
   else if (fused)
     prefill_mfma_kernel<D, HGP, false, true><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
-                                                                     first, 0);
+                                                                     first, 0, 1);
   else
     prefill_mfma_kernel<D, HGP, false, false><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
-                                                                      first, 0);
+                                                                      first, 0, 1);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && dpl) e = launch_decode_merge(a, *dpl, PKV_BF16, st);
   // A shared run's partials are merged with the rows' other parts elsewhere.
