@@ -428,9 +428,10 @@ size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t nu
       num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || dtype != PKV_BF16 ||
       shared_blocks <= 0 || max_context_len < 0)
     return 0;
-  // Decode partials of the private keys, then the shared run's key splits.
+  // Decode partials of the private keys (8-wave workgroups in the shared run's launch),
+  // then the shared run's key splits.
   const DecodePlan dp = plan_decode(num_seqs, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                    max_context_len, dtype, shared_blocks, true);
+                                    max_context_len, dtype, shared_blocks, true, true);
   return plan_shared_run(num_seqs, num_q_heads, num_kv_heads, head_dim,
                          shared_blocks * kBlock, dp.ws_bytes)
       .ws_end;
@@ -469,7 +470,7 @@ pkv_status paged_attention_varlen_shared_prefix(
     return PKV_ERR_INVALID_ARG;
 
   DecodePlan dp = plan_decode(num_seqs, total_q, num_q_heads, num_kv_heads, head_dim,
-                              max_context_len, dtype, shared_blocks, true);
+                              max_context_len, dtype, shared_blocks, true, true);
   PrefillPlan sp = plan_shared_run(total_q, num_q_heads, num_kv_heads, head_dim,
                                    shared_blocks * kBlock, dp.ws_bytes);
   if (!workspace || workspace_bytes < sp.ws_end) return PKV_ERR_WORKSPACE;
@@ -493,16 +494,15 @@ pkv_status paged_attention_varlen_shared_prefix(
   a.head_dim = head_dim;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
-  if (with_write) {  // the decode kernel stores the new rows (all past the shared run)
+  if (with_write) {  // the decode workgroups store the new rows (all past the shared run)
     a.k_new = k_new;
     a.v_new = v_new;
     a.slot_mapping = slot_mapping;
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  // Private keys (each row's own blocks), the shared run once for every row, then the
-  // merge of both parts per row and head.
-  hipError_t e = launch_decode(a, dp, dtype, st);
-  if (e == hipSuccess) e = launch_shared_run(a, sp, shared_blocks * kBlock, st);
+  // The shared run once for every row and the private keys (each row's own blocks) in
+  // one launch, then the merge of both parts per row and head.
+  hipError_t e = launch_shared_run_mixed(a, sp, shared_blocks * kBlock, dp, st);
   if (e == hipSuccess) e = launch_cascade_merge(a, dp, sp, st);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

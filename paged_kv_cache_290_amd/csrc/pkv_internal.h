@@ -191,6 +191,11 @@ constexpr int mixed_decode_head_group(int head_dim, int chunk_head_group) {
   return head_dim == 64 ? chunk_head_group : (chunk_head_group > 2 ? 2 : chunk_head_group);
 }
 // The shared-run pass (prefill kernel in shared-run mode; partials only).
+// The shared-run pass and the private parts' decode workgroups (plan `dp`, planned
+// with cascade and mixed set) in one launch: the shared-run tiles first, then the
+// decode workgroups, which also store a fused call's new rows.
+hipError_t launch_shared_run_mixed(const AttnArgs &a, const PrefillPlan &sp, int shared_keys,
+                                   const DecodePlan &dp, hipStream_t stream);
 hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &p, int shared_keys,
                              hipStream_t stream);
 // Merge of a shared-prefix batch: per (row, q head), the decode pieces of the private

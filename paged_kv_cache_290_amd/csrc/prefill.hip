@@ -408,6 +408,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
         static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
         static_assert(DL::bytes() <= sizeof(lds), "the decode LDS must fit in the tiles");
+        // A shared prefix's fused call: the decode workgroups store the new rows (the
+        // shared-run tiles read none of them; each decode row's newest key and value
+        // come from k_new / v_new).
+        if (a.k_new != nullptr)
+          fused_slot_write<uint16_t, D>(a, u - mix_first, mix_dec, kPThreads);
         const int64_t v =
             mixed_decode_piece(a, dp, u - mix_first, mix_bucket, s_tbl, s_find);
         decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(
@@ -810,8 +815,8 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     ps.lse = reinterpret_cast<float *>(w + pl.ws_lse_offset);
     ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
   }
-  // Fused calls (k_new given) store the new rows in this launch; the shared-run pass
-  // of a shared prefix never does (its decode launch stores them).
+  // Fused calls (k_new given) store the new rows in this launch: the chunk tiles of a
+  // single sequence (FUSED), or the decode workgroups of a shared prefix's launch.
   const bool fused = a.k_new != nullptr && shared_keys == 0;
   const dim3 grid((unsigned)(total + dec_wgs)), block(kPThreads);
   const int nhg = pl.num_head_groups, slots = pl.tile_slots, ndec = (int)dec_wgs;
@@ -862,6 +867,14 @@ hipError_t launch_mixed(const AttnArgs &a, const PrefillPlan &pp, const DecodePl
                         hipStream_t stream) {
   if (a.head_dim == 64) return launch_prefill_d<64>(a, pp, 0, stream, &dp);
   if (a.head_dim == 128) return launch_prefill_d<128>(a, pp, 0, stream, &dp);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shared_run_mixed(const AttnArgs &a, const PrefillPlan &sp, int shared_keys,
+                                   const DecodePlan &dp, hipStream_t stream) {
+  if (shared_keys <= 0) return hipErrorInvalidValue;
+  if (a.head_dim == 64) return launch_prefill_d<64>(a, sp, shared_keys, stream, &dp);
+  if (a.head_dim == 128) return launch_prefill_d<128>(a, sp, shared_keys, stream, &dp);
   return hipErrorInvalidValue;
 }
 
