@@ -350,7 +350,7 @@ __device__ __forceinline__ void tile_update(FM &&mid, const uint4 *kb, const uin
 // workgroups (row tiles that surely exist), the `mix_dec` decode workgroups, then the
 // other chunk workgroups (slots that may be empty), so that the units freed by short
 // row tiles go to decode work rather than to empty slots; mix_bucket is the bucket
-// width (keys) of the decode rows' longest-first order.  Without decode workgroups
+// width (keys) of the decode rows' longest-first order (0: the plan's order).  Without decode workgroups
 // mix_dec is 0 and mix_first the number of row-tile workgroups that surely exist (at
 // least one).
 template <int D, int HGP, bool MIXED, bool FUSED>
@@ -393,12 +393,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
   const int units = a.num_kv_heads * num_head_groups;
   const int total = tile_slots * units * ps.splits;
   int u = blockIdx.x;
-  // FUSED (the chunk launch of a fused call with one sequence): the launch stores this
-  // step's new rows, the first mix_first workgroups a share each (those dispatched
-  // first: the row tiles that surely exist), and the chunk tiles read those keys and
-  // values from k_new / v_new.
-  if constexpr (FUSED) {
-    if ((int)blockIdx.x < mix_first)
+  // Fused calls store this step's new rows in this launch, the first mix_first
+  // workgroups a share each (those dispatched first: the row tiles that surely exist).
+  // FUSED (the chunk launch of a fused call with one sequence): the chunk tiles read
+  // those keys and values from k_new / v_new.  MIXED with k_new (a shared prefix's
+  // fused call): the shared-run tiles read none of them, and each decode row's newest
+  // key and value come from k_new / v_new.  (In the shared-run launch the tiles come
+  // first and end earlier than the second round of decode workgroups, so the write
+  // stays off the launch's longest chain.)
+  if constexpr (FUSED || MIXED) {
+    if ((FUSED || a.k_new != nullptr) && (int)blockIdx.x < mix_first)
       fused_slot_write<uint16_t, D>(a, blockIdx.x, mix_first, kPThreads);
   }
   if constexpr (MIXED) {
@@ -408,13 +412,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(AttnArgs a,
         using DL = DecodeLds<uint16_t, D, HGD, kDecodeWavesMin>;
         static_assert(kPThreads == 64 * kDecodeWavesMin, "one decode workgroup per workgroup");
         static_assert(DL::bytes() <= sizeof(lds), "the decode LDS must fit in the tiles");
-        // A shared prefix's fused call: the decode workgroups store the new rows (the
-        // shared-run tiles read none of them; each decode row's newest key and value
-        // come from k_new / v_new).
-        if (a.k_new != nullptr)
-          fused_slot_write<uint16_t, D>(a, u - mix_first, mix_dec, kPThreads);
+        // Longest rows first (mix_bucket > 0), else in the plan's order.
         const int64_t v =
-            mixed_decode_piece(a, dp, u - mix_first, mix_bucket, s_tbl, s_find);
+            mix_bucket > 0 ? mixed_decode_piece(a, dp, u - mix_first, mix_bucket, s_tbl, s_find)
+                           : (int64_t)(u - mix_first);
         decode_segment<uint16_t, D, HGD, kDecodeWavesMin>(
             a, dp, v, DL::over(reinterpret_cast<char *>(lds)));
         return;
@@ -805,6 +806,8 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
       total, (int64_t)std::min(sure, pl.tile_slots) * a.num_kv_heads * pl.num_head_groups *
                  pl.splits);
   if (total + dec_wgs > INT32_MAX) return hipErrorInvalidValue;
+  // The new rows of a fused call are stored by the first `first` workgroups.
+  if (a.k_new != nullptr && first == 0) return hipErrorInvalidValue;
   if (total + dec_wgs == 0) return hipSuccess;
   PrefillSplit ps{};
   ps.splits = pl.splits;
@@ -825,8 +828,11 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
   // the new rows cost more than the separate write launch they save.
   if (dpl && fused) return hipErrorInvalidValue;
   // Buckets of the decode rows' longest-first order: 254 of them over the longest
-  // context (a longer row falls in the first).
-  const int bucket = std::max(1, (dpl ? dpl->max_context_len : 0) / 254 + 1);
+  // context (a longer row falls in the first).  A shared run's decode rows (the
+  // private tails, all short) keep the plan's order: the order costs each decode
+  // workgroup a dependent read of every row's lengths, on the launch's longest chain.
+  const int bucket =
+      shared_keys > 0 ? 0 : std::max(1, (dpl ? dpl->max_context_len : 0) / 254 + 1);
   if (dpl)
     prefill_mfma_kernel<D, HGP, true, false><<<grid, block, 0, st>>>(a, nhg, slots, ps, dp,
                                                                      first, ndec, bucket);
