@@ -199,9 +199,10 @@ pkv_status paged_attention_varlen_with_write(
  * num_seqs); other shapes give PKV_ERR_UNSUPPORTED before any launch (use the plain
  * entry points).  The workspace query takes the call's max_context_len.  Two
  * launches on `stream`: one of the MFMA chunk kernel, whose first workgroups run the
- * shared blocks with every row as a column (partial results per key split) and whose
- * other workgroups run the decode work over each row's own blocks (partial results;
- * a fused call's new rows are stored there), then a merge per (row, query head).
+ * shared blocks with every row as a column (partial results per key split; these also
+ * store a fused call's new rows, which no part of the launch reads from the pools) and
+ * whose other workgroups run the decode work over each row's own blocks (partial
+ * results), then a merge per (row, query head).
  */
 size_t paged_attention_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
