@@ -96,7 +96,7 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_pool,
  * batch and for invalid shapes.  Its size depends on the device's compute-unit count.
  * For bf16 batches of several sequences with more query rows than sequences (so
  * holding a chunk) it also covers the key ranges of the decode rows when they run in
- * the chunk launch (8-wave workgroups: rows past 2,048 keys are cut into ranges).
+ * the chunk launch (8-wave workgroups: rows past 4,096 keys are cut into ranges).
  * The shape arguments must match the later call.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q,

@@ -63,11 +63,12 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
   p.waves = (dtype == PKV_BF16 && segments <= cus && !mixed) ? kDecodeWavesMax
                                                               : kDecodeWavesMin;
   // Key ranges per segment: one, unless a wave would take more than kBlocksPerWave
-  // blocks of the longest row, or the segments alone leave compute units idle (then
-  // as many as fill them, each range keeping a block per wave or more).
+  // (kMixedBlocksPerWave in a mixed launch) blocks of the longest row, or the segments
+  // alone leave compute units idle (then as many as fill them, each range keeping a
+  // block per wave or more).
   const int64_t nb = std::max<int64_t>(
       (max_context_len + kBlock - 1) / kBlock - (int64_t)skip_blocks, 1);
-  const int64_t cap = (int64_t)p.waves * kBlocksPerWave;
+  const int64_t cap = (int64_t)p.waves * (mixed ? kMixedBlocksPerWave : kBlocksPerWave);
   int64_t splits = (nb + cap - 1) / cap;
   if (segments > 0 && segments * splits < cus) {
     const int64_t fill = (cus + segments - 1) / segments;

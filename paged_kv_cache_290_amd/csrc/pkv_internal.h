@@ -78,6 +78,10 @@ int32_t append_unchecked(pkv_block_allocator *a, int32_t *table, int32_t context
 constexpr int kDecodeWavesMax = 16;  // waves per decode workgroup: 16 when the
 constexpr int kDecodeWavesMin = 8;   // segments fit the compute units one each, else 8
 constexpr int kBlocksPerWave = 16;   // blocks a wave may take before segments split
+// The same bound for the decode rows of a mixed launch: those run longest first after
+// the chunk tiles, so longer pieces start early, and rows up to 4,096 keys then need
+// no key ranges (no merge launch).
+constexpr int kMixedBlocksPerWave = 32;
 
 struct DecodePlan {
   int items;            // work rows: num_seqs (bf16) or total_q (fp32)

@@ -124,10 +124,12 @@ def test_workspace_size_plan():
     # a chunk with few tiles over a long context: split partials
     assert ws(1, 40, 16, 8, 128, 6000, _lib.PKV_BF16) > 0
     # several sequences with more rows than sequences (a chunk and decode rows): the
-    # decode rows run in the chunk launch's 8-wave workgroups, so rows past 2,048 keys
-    # are cut into key ranges; with as many rows as sequences the plain plan applies
+    # decode rows run in the chunk launch's 8-wave workgroups, up to 32 blocks a wave,
+    # so rows past 4,096 keys are cut into key ranges; with as many rows as sequences
+    # the plain plan applies
     assert ws(32, 2048, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
-    assert ws(32, 2048, 16, 8, 128, 4096, _lib.PKV_BF16) > 0
+    assert ws(32, 2048, 16, 8, 128, 4096, _lib.PKV_BF16) == 0
+    assert ws(32, 2048, 16, 8, 128, 4097, _lib.PKV_BF16) > 0
     assert ws(32, 32, 16, 8, 128, 4096, _lib.PKV_BF16) == 0
     assert ws(0, 0, 32, 8, 64, 2048, _lib.PKV_BF16) == 0
     assert ws(4, 4, 6, 4, 64, 2048, _lib.PKV_BF16) == 0       # invalid heads
