@@ -1070,8 +1070,9 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not "
-              "part of it (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py: the library and this benchmark run on exactly one GPU; there is "
+              "no multi-GPU path (decode would shard by sequence or by kv head, with no "
+              "exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
