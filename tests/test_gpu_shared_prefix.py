@@ -150,3 +150,66 @@ def test_unsupported_shapes_are_rejected():
                                     dbf.context_lens, dbf.query_start_loc, shared_blocks=2,
                                     scale=f.scale, max_context_len=f.max_context_len)
     assert ei.value.status == _lib.PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_cascade_graph_replays_follow_new_metadata(fused):
+    """A serving loop captures the shared-prefix step once and replays it with new
+    values in the same device buffers: other shared blocks, other private tails, new
+    queries, rows and slots, under the same host hints (shared run, maximum context)
+    and shapes.  Every replay must equal the oracle on that replay's inputs, pools bit
+    for bit (the fused call stores the new rows inside the captured launch)."""
+    hq, hkv, d, shared, rows, nb = 16, 8, 128, 40, 12, 400
+    max_ctx = shared * 16 + 200
+    max_blocks = (max_ctx + 15) // 16
+
+    def case(seed):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        tails = rng.integers(1, 200, size=rows, endpoint=True)
+        return make_batch(rng, name=f"cascade_replay{seed}", dtype="bf16", num_q_heads=hq,
+                          num_kv_heads=hkv, head_dim=d, num_blocks=nb,
+                          context_lens=shared * 16 + tails, query_lens=[1] * rows,
+                          shared_prefix_blocks=shared, max_blocks_per_seq=max_blocks,
+                          stale="nan")
+
+    print(f"[case] cascade graph over changing metadata, fused={fused}", flush=True)
+    b0 = case(200)
+    db = DeviceBatch(b0)
+    out = torch.empty_like(db.q)
+    ws = torch.empty(pkv.shared_prefix_workspace_size(rows, hq, hkv, d, max_ctx, shared),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        kw = dict(shared_blocks=shared, scale=b0.scale, max_context_len=max_ctx, out=out,
+                  workspace=ws)
+        if fused:
+            kw.update(k_new=db.k_new, v_new=db.v_new, slot_mapping=db.slot_mapping)
+        else:
+            pkv.kv_write(db.k_new, db.v_new, db.k_pool, db.v_pool, db.slot_mapping)
+        pkv.attention_shared_prefix(db.q, db.k_pool, db.v_pool, db.block_tables,
+                                    db.context_lens, db.query_start_loc, **kw)
+
+    step()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+
+    for seed in (201, 202, 203):
+        b = case(seed)
+        src = DeviceBatch(b)
+        for f in ("k_pool", "v_pool", "q", "k_new", "v_new", "block_tables", "context_lens",
+                  "query_start_loc", "slot_mapping"):
+            getattr(db, f).copy_(getattr(src, f))
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        kp, vp, ref = O.step(b)
+        assert to_raw(db.k_pool).tobytes() == kp.tobytes(), f"K pool after replay {seed}"
+        assert to_raw(db.v_pool).tobytes() == vp.tobytes(), f"V pool after replay {seed}"
+        _assert_close(b, out_f64(out), ref, f"cascade replay {seed}")
