@@ -64,15 +64,19 @@ DecodePlan plan_decode(int num_seqs, int total_q, int num_q_heads, int num_kv_he
                                                               : kDecodeWavesMin;
   // Key ranges per segment: one, unless a wave would take more than kBlocksPerWave
   // (kMixedBlocksPerWave in a mixed launch) blocks of the longest row, or the segments
-  // alone leave compute units idle (then as many as fill them, each range keeping a
-  // block per wave or more).
+  // leave at least half of the compute units idle and the longest row gives every
+  // wave 4 blocks or more (then as many ranges as fit the units in one round,
+  // floor(cus / segments), each keeping a block per wave or more).  A second round
+  // of workgroups, or a merge launch for a chip that is nearly full or for rows whose
+  // workgroups are short chains of round trips, costs more than the idle units.
   const int64_t nb = std::max<int64_t>(
       (max_context_len + kBlock - 1) / kBlock - (int64_t)skip_blocks, 1);
   const int64_t cap = (int64_t)p.waves * (mixed ? kMixedBlocksPerWave : kBlocksPerWave);
   int64_t splits = (nb + cap - 1) / cap;
   if (segments > 0 && segments * splits < cus) {
-    const int64_t fill = (cus + segments - 1) / segments;
-    const int64_t keep = (nb + p.waves - 1) / p.waves;  // ranges with >= 1 block per wave
+    const int64_t fill = cus / segments;
+    const int64_t keep =  // ranges with >= 1 block per wave, for long rows only
+        nb >= 4 * (int64_t)p.waves ? (nb + p.waves - 1) / p.waves : 1;
     splits = std::max(splits, std::min(fill, keep));
   }
   p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(splits, 1 << 16));
@@ -94,13 +98,14 @@ PrefillPlan plan_prefill(int num_seqs, int total_q, int num_q_heads, int num_kv_
   p.num_head_groups = group / p.head_group;
   p.tile_slots = prefill_tile_slots(total_q, num_seqs, kPrefillCols / p.head_group);
   p.tiles = p.tile_slots * num_kv_heads * p.num_head_groups;
-  // Split the key range when the tiles cannot fill the compute units, keeping at
-  // least two of the kernel's key steps per split.
+  // Split the key range when the tiles leave at least half of the compute units idle,
+  // into as many splits as fit them in one round, keeping at least two of the kernel's
+  // key steps per split.
   const int cus = device_cus();
   const int steps = (max_context_len + kPrefillStepKeys - 1) / kPrefillStepKeys;
   p.splits = 1;
   if (dtype == PKV_BF16 && p.tiles > 0 && p.tiles < cus && steps >= 4)
-    p.splits = std::max(1, std::min((cus + p.tiles - 1) / p.tiles, steps / 2));
+    p.splits = std::max(1, std::min(cus / p.tiles, steps / 2));
   p.ws_end = ws_offset;
   if (p.splits > 1) {
     const size_t parts = (size_t)p.tiles * p.splits * kPrefillCols;

@@ -220,8 +220,8 @@ void validator_and_arguments() {
          PKV_ERR_WORKSPACE);
   EXPECT(paged_attention_shared_prefix_workspace_size(2, 8, 4, 64, 30, 1, PKV_BF16) > 64);
   // The no-alloc call: a batch beyond its scratch is refused before any device call.
-  EXPECT(paged_attention_varlen_with_write_noalloc(p, p, p, p, p, p, slots, bt, ctx, qsl, 1,
-                                                   32512, 8, 4, 32512, 32512, 1, 1, 128, 16,
+  EXPECT(paged_attention_varlen_with_write_noalloc(p, p, p, p, p, p, slots, bt, ctx, qsl, 256,
+                                                   256, 8, 4, 32768, 1, 16, 8, 128, 16,
                                                    0.125f, PKV_BF16, nullptr) ==
          PKV_ERR_WORKSPACE);
 }

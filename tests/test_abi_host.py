@@ -115,8 +115,15 @@ def test_workspace_size_plan():
     long1 = ws(32, 32, 32, 8, 64, 4097, _lib.PKV_BF16)
     assert long1 > 0
     assert ws(64, 64, 32, 8, 64, 4097, _lib.PKV_BF16) > long1   # grows with rows
-    # few segments: ranges to fill the GPU
+    # few segments: ranges to fill the GPU in one round, floor(256 / segments) each,
+    # only once at least half the units would idle and for rows of 4+ blocks a wave
+    # (30 x 8 = 240 segments: none; 16 x 8 = 128 of 2,048 keys: two ranges each; of
+    # 384 keys, too short to split, and no chunk can split over 3 key steps: none)
     assert ws(2, 2, 8, 2, 64, 2048, _lib.PKV_BF16) > 0
+    assert ws(30, 30, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
+    assert ws(16, 16, 16, 8, 128, 2048, _lib.PKV_BF16) > 0
+    assert ws(17, 17, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
+    assert ws(16, 16, 16, 8, 128, 384, _lib.PKV_BF16) == 0
     few = ws(2, 2, 8, 2, 64, 2048, _lib.PKV_F32)
     assert few > 0
     assert ws(2, 8, 8, 2, 64, 2048, _lib.PKV_F32) > few         # fp32 items are rows
@@ -179,8 +186,8 @@ def test_noalloc_entry_point_rejects_beyond_its_scratch():
                   max_q, hq, hkv, d, bs, 0.125, dtype, None)
 
     ws = lib.paged_attention_workspace_size
-    assert ws(1, 32512, 1, 1, 128, 32512, _lib.PKV_BF16) > (32 << 20)
-    assert call(1, 32512, 1, 1, 128, 32512, 32512) == _lib.PKV_ERR_WORKSPACE
+    assert ws(256, 256, 16, 8, 128, 32768, _lib.PKV_BF16) > (32 << 20)
+    assert call(256, 256, 16, 8, 128, 32768, 1) == _lib.PKV_ERR_WORKSPACE
     assert ws(2048, 2048, 32, 32, 128, 4096, _lib.PKV_F32) > (32 << 20)
     assert call(2048, 2048, 32, 32, 128, 4096, 1, _lib.PKV_F32) == _lib.PKV_ERR_WORKSPACE
     assert call(1, 32512, 1, 1, 96, 32512, 32512) == _lib.PKV_ERR_UNSUPPORTED

@@ -19,8 +19,9 @@ from workloads import make_batch, make_config
 pytestmark = pytest.mark.gpu
 
 
-def _noalloc(db, out):
-    """Direct C-ABI call of the no-alloc entry point on the current stream."""
+def _noalloc(db, out, max_context_len=None):
+    """Direct C-ABI call of the no-alloc entry point on the current stream (the host
+    hint max_context_len defaults to the batch's own)."""
     b = db.b
     lib = _lib.load()
     st = lib.paged_attention_varlen_with_write_noalloc(
@@ -28,7 +29,8 @@ def _noalloc(db, out):
         db.k_pool.data_ptr(), db.v_pool.data_ptr(), db.slot_mapping.data_ptr(),
         db.block_tables.data_ptr(), db.context_lens.data_ptr(),
         db.query_start_loc.data_ptr(), b.num_seqs, b.total_q, b.num_blocks,
-        b.max_blocks_per_seq, b.max_context_len, b.max_query_len, b.num_q_heads,
+        b.max_blocks_per_seq, max_context_len or b.max_context_len, b.max_query_len,
+        b.num_q_heads,
         b.num_kv_heads, b.head_dim, 16, ctypes.c_float(b.scale),
         _lib.PKV_BF16 if b.dtype == "bf16" else _lib.PKV_F32,
         torch.cuda.current_stream().cuda_stream)
@@ -85,20 +87,20 @@ def test_noalloc_equals_workspace_entry_point(name):
 
 
 def test_noalloc_rejects_a_call_beyond_its_scratch():
-    """A batch whose partials need more than the scratch holds (a 32,512-row chunk in
-    255 tiles, each split in two): PKV_ERR_WORKSPACE, no launch, the output and the
-    pools left untouched."""
+    """A batch whose partials would need more than the scratch holds (256 decode rows,
+    16q/8kv, d=128, under a 32,768-key host hint: every row in 16 key ranges):
+    PKV_ERR_WORKSPACE, no launch, the output and the pools left untouched."""
     print("[case] noalloc too large", flush=True)
-    b = _small(25, dtype="bf16", num_q_heads=1, num_kv_heads=1, head_dim=128,
-               num_blocks=2040, context_lens=[32512], query_lens=[32512])
-    need = pkv.workspace_size(b.num_seqs, b.total_q, 1, 1, 128, b.max_context_len,
-                              torch.bfloat16)
+    b = _small(25, dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128,
+               num_blocks=300, context_lens=[9] * 256, query_lens=[1] * 256)
+    hint = 32768
+    need = pkv.workspace_size(b.num_seqs, b.total_q, 16, 8, 128, hint, torch.bfloat16)
     assert need > (32 << 20)
     db = DeviceBatch(b)
     before = to_raw(db.k_pool).tobytes()
     out = torch.full_like(db.q, 7.0)
     with pytest.raises(pkv.PagedKVError) as ei:
-        _noalloc(db, out)
+        _noalloc(db, out, max_context_len=hint)
     assert ei.value.status == _lib.PKV_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
