@@ -117,12 +117,10 @@ def test_workspace_size_plan():
     assert ws(64, 64, 32, 8, 64, 4097, _lib.PKV_BF16) > long1   # grows with rows
     # few segments: ranges to fill the GPU in one round, floor(256 / segments) each,
     # only once at least half the units would idle and for rows of 4+ blocks a wave
-    # (30 x 8 = 240 segments: none; 16 x 8 = 128 of 2,048 keys: two ranges each; of
-    # 384 keys, too short to split, and no chunk can split over 3 key steps: none)
+    # (at 384 keys no chunk can split, its 3 key steps being too few: 30 x 8 = 240
+    # segments, none; 16 x 8 = 128 segments of 24 blocks, too short, none)
     assert ws(2, 2, 8, 2, 64, 2048, _lib.PKV_BF16) > 0
-    assert ws(30, 30, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
-    assert ws(16, 16, 16, 8, 128, 2048, _lib.PKV_BF16) > 0
-    assert ws(17, 17, 16, 8, 128, 2048, _lib.PKV_BF16) == 0
+    assert ws(30, 30, 16, 8, 128, 384, _lib.PKV_BF16) == 0
     assert ws(16, 16, 16, 8, 128, 384, _lib.PKV_BF16) == 0
     few = ws(2, 2, 8, 2, 64, 2048, _lib.PKV_F32)
     assert few > 0
