@@ -502,7 +502,7 @@ pkv_status paged_attention_varlen_shared_prefix(
   a.head_dim = head_dim;
   a.max_query_len = max_query_len;
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
-  if (with_write) {  // the decode workgroups store the new rows (all past the shared run)
+  if (with_write) {  // the shared-run tiles store the new rows (all past the shared run)
     a.k_new = k_new;
     a.v_new = v_new;
     a.slot_mapping = slot_mapping;

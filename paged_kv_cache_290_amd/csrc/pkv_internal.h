@@ -194,14 +194,12 @@ hipError_t launch_mixed(const AttnArgs &a, const PrefillPlan &pp, const DecodePl
 constexpr int mixed_decode_head_group(int head_dim, int chunk_head_group) {
   return head_dim == 64 ? chunk_head_group : (chunk_head_group > 2 ? 2 : chunk_head_group);
 }
-// The shared-run pass (prefill kernel in shared-run mode; partials only).
-// The shared-run pass and the private parts' decode workgroups (plan `dp`, planned
-// with cascade and mixed set) in one launch: the shared-run tiles first, then the
-// decode workgroups, which also store a fused call's new rows.
+// The shared-run pass (the prefill kernel in shared-run mode, partials only) and the
+// private parts' decode workgroups (plan `dp`, planned with cascade and mixed set) in
+// one launch: the shared-run tiles first (they also store a fused call's new rows),
+// then the decode workgroups.
 hipError_t launch_shared_run_mixed(const AttnArgs &a, const PrefillPlan &sp, int shared_keys,
                                    const DecodePlan &dp, hipStream_t stream);
-hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &p, int shared_keys,
-                             hipStream_t stream);
 // Merge of a shared-prefix batch: per (row, q head), the decode pieces of the private
 // part (plan `dp`, launched with cascade set) and the shared run's splits (plan `sp`).
 hipError_t launch_cascade_merge(const AttnArgs &a, const DecodePlan &dp,

@@ -819,7 +819,7 @@ static hipError_t launch_prefill_t(const AttnArgs &a, const PrefillPlan &pl, int
     ps.col = reinterpret_cast<int *>(w + pl.ws_col_offset);
   }
   // Fused calls (k_new given) store the new rows in this launch: the chunk tiles of a
-  // single sequence (FUSED), or the decode workgroups of a shared prefix's launch.
+  // single sequence (FUSED), or the shared-run tiles of a shared prefix's launch.
   const bool fused = a.k_new != nullptr && shared_keys == 0;
   const dim3 grid((unsigned)(total + dec_wgs)), block(kPThreads);
   const int nhg = pl.num_head_groups, slots = pl.tile_slots, ndec = (int)dec_wgs;
@@ -881,14 +881,6 @@ hipError_t launch_shared_run_mixed(const AttnArgs &a, const PrefillPlan &sp, int
   if (shared_keys <= 0) return hipErrorInvalidValue;
   if (a.head_dim == 64) return launch_prefill_d<64>(a, sp, shared_keys, stream, &dp);
   if (a.head_dim == 128) return launch_prefill_d<128>(a, sp, shared_keys, stream, &dp);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_shared_run(const AttnArgs &a, const PrefillPlan &pl, int shared_keys,
-                             hipStream_t stream) {
-  if (shared_keys <= 0) return hipErrorInvalidValue;
-  if (a.head_dim == 64) return launch_prefill_d<64>(a, pl, shared_keys, stream);
-  if (a.head_dim == 128) return launch_prefill_d<128>(a, pl, shared_keys, stream);
   return hipErrorInvalidValue;
 }
 
